@@ -1,0 +1,146 @@
+// C-ABI host layer of libfa: argument validation, kernel selection and
+// launch on the caller's stream. Declarations and the contract of every
+// entry point are in include/fa.h.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxI32 = 2147483647;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check(const fa_params* p) {
+  if (p == nullptr) return FA_ERR_NULL;
+  if (p->B < 0 || p->H < 0 || p->N < 0 || p->d < 0) return FA_ERR_SHAPE;
+  if (p->d != 64 && p->d != 128) return FA_ERR_HEADDIM;
+  if (p->in_dtype < FA_F32 || p->in_dtype > FA_BF16) return FA_ERR_DTYPE;
+  if (p->grad_dtype != FA_F32 && p->grad_dtype != p->in_dtype) return FA_ERR_DTYPE;
+  // Per-head element offsets are 32-bit; the grid is one dimension.
+  if (p->N > kMaxI32 / p->d) return FA_ERR_SHAPE;
+  if (p->B > 0 && p->H > kMaxI32 / p->B) return FA_ERR_SHAPE;
+  const int64_t bh = p->B * p->H;
+  const int64_t tiles = (p->N + 127) / 128;
+  if (bh > 0 && tiles > kMaxI32 / bh) return FA_ERR_SHAPE;
+  if (!std::isfinite(p->scale) || !(p->scale > 0.f)) return FA_ERR_SCALE;
+  if (!(p->dropout_p >= 0.0 && p->dropout_p < 1.0)) return FA_ERR_DROPOUT;
+  if (p->block_mask != nullptr && (p->mask_block <= 0 || p->mask_block % 128 != 0)) return FA_ERR_MASK;
+  return FA_OK;
+}
+
+fa::AttnArgs make_args(const fa_params* p) {
+  fa::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.N = (int)p->N;
+  a.H = (int)p->H;
+  a.BH = (int)(p->B * p->H);
+  a.causal = p->causal ? 1 : 0;
+  a.bmask = p->block_mask;
+  a.mask_block = p->block_mask ? p->mask_block : 128;
+  a.nb = (int)((p->N + a.mask_block - 1) / a.mask_block);
+  a.scale = p->scale;
+  a.sl2 = (float)((double)p->scale * 1.4426950408889634);
+  a.rp = (float)(1.0 / (1.0 - p->dropout_p));
+  a.thresh = (uint32_t)std::floor(p->dropout_p * 4294967296.0);
+  a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFu);
+  a.seed_hi = (uint32_t)(p->seed >> 32);
+  return a;
+}
+
+fa::Elt elt(int32_t t) { return static_cast<fa::Elt>(t); }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid or too large shape (B, H, N)";
+    case FA_ERR_DTYPE: return "unsupported dtype combination";
+    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_DROPOUT: return "dropout_p must lie in [0, 1)";
+    case FA_ERR_MASK: return "mask_block must be a positive multiple of 128";
+    case FA_ERR_ALIGN: return "data pointers must be 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP runtime error at launch";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_RANGE: return "window outside [0, N) or (b, h) outside [0, B) x [0, H)";
+    default: return "unknown status";
+  }
+}
+
+int fa_check_params(const fa_params* p) { return check(p); }
+
+int fa_fwd(const fa_params* p, const void* Q, const void* K, const void* V, void* O, float* LSE, void* stream) {
+  const int st = check(p);
+  if (st != FA_OK) return st;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_ALIGN;
+  if (p->B * p->H * p->N == 0) return FA_OK;
+  fa::AttnArgs a = make_args(p);
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.out = O;
+  a.lse = LSE;
+  const hipError_t e = fa::launch_fwd(elt(p->in_dtype), (int)p->d, a.thresh != 0, a, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(const fa_params* p) {
+  if (check(p) != FA_OK) return 0;
+  const size_t rows = (size_t)(p->B * p->H * p->N);
+  return (rows * sizeof(float) + 255) / 256 * 256;
+}
+
+int fa_bwd(const fa_params* p, const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+           const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check(p);
+  if (st != FA_OK) return st;
+  if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV) return FA_ERR_NULL;
+  const void* ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV};
+  for (const void* x : ptrs)
+    if (!aligned16(x)) return FA_ERR_ALIGN;
+  const size_t need = fa_bwd_workspace_bytes(p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  if (workspace != nullptr && !aligned16(workspace)) return FA_ERR_ALIGN;
+  if (p->B * p->H * p->N == 0) return FA_OK;
+  fa::AttnArgs a = make_args(p);
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.o = O;
+  a.lse = const_cast<float*>(LSE);
+  a.dout = dO;
+  a.dq = dQ;
+  a.dk = dK;
+  a.dv = dV;
+  a.delta = static_cast<float*>(workspace);
+  const hipError_t e = fa::launch_bwd(elt(p->in_dtype), elt(p->grad_dtype), (int)p->d, a.thresh != 0, a,
+                                      (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_dropout_mask(const fa_params* p, int64_t b, int64_t h, int64_t i0, int64_t rows, int64_t j0, int64_t cols,
+                    uint8_t* keep, void* stream) {
+  const int st = check(p);
+  if (st != FA_OK) return st;
+  if (keep == nullptr) return FA_ERR_NULL;
+  if (b < 0 || b >= p->B || h < 0 || h >= p->H) return FA_ERR_RANGE;
+  if (i0 < 0 || rows < 0 || j0 < 0 || cols < 0 || i0 + rows > p->N || j0 + cols > p->N) return FA_ERR_RANGE;
+  if (rows > 0 && cols > kMaxI32 * 256 / rows) return FA_ERR_RANGE;
+  if (rows * cols == 0) return FA_OK;
+  const fa::AttnArgs a = make_args(p);
+  const hipError_t e = fa::launch_dropout_mask(a, (int)b, (int)h, i0, rows, j0, cols, keep, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,501 @@
+// Backward pass of tiled exact attention for gfx950.
+//
+// Only O and the per-row log-sum-exp were kept from the forward; S and P
+// are recomputed tile by tile on chip from Q, K and LSE (FlashAttention
+// milestone page, "The idea", recomputation; pixelation article, "The
+// Recomputation Trade-off"). The gradients follow from the chain rule on the
+// forward definition, with Pd = P * Z / (1 - p):
+//   dV = Pd^T dO,  dP = (dO V^T) * Z / (1 - p),  D_i = dO_i . O_i,
+//   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// Two kernels, both deterministic (no atomics):
+//   bwd_dq_kernel   one workgroup per 128 query rows: D_i (written to the
+//                   workspace), then a loop over K/V tiles accumulating dQ.
+//                   Mirrors the forward's orientation (S^T = K Q^T, lanes
+//                   own a query), so dS^T is directly the B operand of
+//                   dQ^T += K^T dS^T; K^T is read from the row-major K tile
+//                   with LDS transpose reads.
+//   bwd_dkdv_kernel one workgroup per 128 key rows: a loop over Q tiles in
+//                   the orientation S = Q K^T (lanes own a key), so P and dS
+//                   are directly the B operands of dV^T += dO^T P and
+//                   dK^T += Q^T dS; dO^T and Q^T come from the row-major
+//                   tiles through LDS transpose reads.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+template <typename T, int D>
+struct TileShape {
+  static constexpr int EPC = 16 / sizeof(T);                // elements per 16-byte chunk
+  static constexpr int KS = D + (sizeof(T) == 2 ? 8 : 4);   // LDS row stride (elements)
+  static constexpr int KCH = D / EPC;                       // 16-byte chunks per row
+};
+
+// ---------------------------------------------------------------------------
+// dQ (and D_i)
+// ---------------------------------------------------------------------------
+template <typename T, typename G, int D, int BC, bool DROP>
+__global__ void __launch_bounds__(256) bwd_dq_kernel(AttnArgs a) {
+  using S = TileShape<T, D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr int KI = M::KI, KH = M::KH;
+  constexpr int BR = 128;
+  constexpr int NKB = BC / 32, NDB = D / 32, NC = D / KI;
+  constexpr int NLD = BC * S::KCH / 256;
+  constexpr int TILE = BC * S::KS;
+  static_assert((BC * S::KCH) % 256 == 0, "tile shape");
+  constexpr float NEG_INF = -__builtin_inff(), POS_INF = __builtin_inff();
+
+  __shared__ __attribute__((aligned(16))) T smem[2][2 * TILE];  // [buffer][K tile | V tile]
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lo = lane & 31, hi = lane >> 5;
+  const int N = a.N;
+  const int nq = (N + BR - 1) / BR;
+  const int rank = blockIdx.x / a.BH;
+  const int bh = blockIdx.x - rank * a.BH;
+  const int qt = a.causal ? (nq - 1 - rank) : rank;
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const T* __restrict__ Qg = static_cast<const T*>(a.q) + hoff;
+  const T* __restrict__ Kg = static_cast<const T*>(a.k) + hoff;
+  const T* __restrict__ Vg = static_cast<const T*>(a.v) + hoff;
+  const T* __restrict__ Og = static_cast<const T*>(a.o) + hoff;
+  const T* __restrict__ dOg = static_cast<const T*>(a.dout) + hoff;
+  G* __restrict__ dQg = static_cast<G*>(a.dq) + hoff;
+
+  const int qtile0 = qt * BR;
+  const int q0w = qtile0 + w * 32;
+  const int q = q0w + lo;
+  const bool qvalid = q < N;
+
+  frag qf[NC], dof[NC];
+  float dpart = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int off = q * D + c * KI + hi * KH;
+    if (qvalid) {
+      qf[c] = load_frag<T>(Qg + off);
+      dof[c] = load_frag<T>(dOg + off);
+      const frag of = load_frag<T>(Og + off);
+      if constexpr (KH == 8) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dpart += to_f32<T>(dof[c][t]) * to_f32<T>(of[t]);
+      } else {
+        dpart += dof[c] * of;
+      }
+    } else {
+      qf[c] = zero_frag<T>();
+      dof[c] = zero_frag<T>();
+    }
+  }
+  const float Dq = dpart + swap_halves(dpart);
+  float lse2 = POS_INF;  // rows without a valid key (LSE = -inf) and padding rows get P = 0
+  if (qvalid) {
+    const float l = a.lse[(size_t)bh * N + q];
+    lse2 = (l == NEG_INF) ? POS_INF : l * kLog2e;
+    if (hi == 0) a.delta[(size_t)bh * N + q] = Dq;
+  }
+  uint32_t rowhash = 0;
+  if constexpr (DROP) {
+    const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
+    rowhash = fmix32(hk ^ (uint32_t)q);
+  }
+
+  const int kend = a.causal ? min(N, qtile0 + BR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+  const uint8_t* bmrow = a.bmask ? a.bmask + (size_t)(qtile0 / a.mask_block) * a.nb : nullptr;
+  auto kept = [&](int j) { return bmrow == nullptr || bmrow[(j * BC) / a.mask_block] != 0; };
+  auto next_kept = [&](int j) {
+    ++j;
+    while (j < ntiles && !kept(j)) ++j;
+    return j;
+  };
+
+  u32x4 kreg[NLD], vreg[NLD];
+  auto gload = [&](int jt) {
+    const int k0 = jt * BC;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = i * 256 + tid;
+      const int row = c / S::KCH, ch = c % S::KCH;
+      const int key = k0 + row;
+      const size_t off = (size_t)key * D + ch * S::EPC;
+      kreg[i] = key < N ? *reinterpret_cast<const u32x4*>(Kg + off) : u32x4{0, 0, 0, 0};
+      vreg[i] = key < N ? *reinterpret_cast<const u32x4*>(Vg + off) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = i * 256 + tid;
+      const int row = c / S::KCH, ch = c % S::KCH;
+      *reinterpret_cast<u32x4*>(&smem[buf][row * S::KS + ch * S::EPC]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&smem[buf][TILE + row * S::KS + ch * S::EPC]) = vreg[i];
+    }
+  };
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dq[db] = zero16();
+
+  int j = kept(0) ? 0 : next_kept(0);
+  int cur = 0;
+  if (j < ntiles) {
+    gload(j);
+    sstore(0);
+  }
+  __syncthreads();
+
+  while (j < ntiles) {
+    const int jn = next_kept(j);
+    if (jn < ntiles) gload(jn);
+    const T* Ks = &smem[cur][0];
+    const T* Vs = &smem[cur][TILE];
+    const int k0 = j * BC;
+    const bool active = (q0w < N) && (!a.causal || k0 <= q0w + 31);
+    if (active) {
+      f32x16 s[NKB], dp[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = zero16();
+        dp[kb] = zero16();
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const int off = (kb * 32 + lo) * S::KS + c * KI + hi * KH;
+          s[kb] = M::run(load_frag<T>(Ks + off), qf[c], s[kb]);
+          dp[kb] = M::run(load_frag<T>(Vs + off), dof[c], dp[kb]);
+        }
+      const bool need_mask = (a.causal && k0 + BC - 1 > q0w) || (k0 + BC > N);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = k0 + kb * 32 + crow(v, hi);
+            if (key >= N || (a.causal && key > q)) s[kb][v] = NEG_INF;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = exp2_fast(fmaf(s[kb][v], a.sl2, -lse2));
+          float dpv = dp[kb][v];
+          if constexpr (DROP) {
+            const uint32_t key = (uint32_t)(k0 + kb * 32 + crow(v, hi));
+            dpv = fmix32(rowhash ^ key) >= a.thresh ? dpv * a.rp : 0.f;
+          }
+          s[kb][v] = p * (dpv - Dq);  // dS^T
+        }
+      if constexpr (KH == 8) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const frag b = pack8<T>(s[kb][8 * hf + 0], s[kb][8 * hf + 1], s[kb][8 * hf + 2], s[kb][8 * hf + 3],
+                                    s[kb][8 * hf + 4], s[kb][8 * hf + 5], s[kb][8 * hf + 6], s[kb][8 * hf + 7]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+              dq[db] = M::run(load_frag_tr<T>(Ks, S::KS, kb * 32 + 16 * hf, db * 32, lane), b, dq[db]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kl = kb * 32 + crow(v, hi);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) dq[db] = M::run(Ks[kl * S::KS + db * 32 + lo], s[kb][v], dq[db]);
+          }
+      }
+    }
+    if (jn < ntiles) sstore(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+    j = jn;
+  }
+
+  if (qvalid) {
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4<G>(dQg + q * D + db * 32 + 8 * g + 4 * hi, dq[db][4 * g] * sc, dq[db][4 * g + 1] * sc,
+                  dq[db][4 * g + 2] * sc, dq[db][4 * g + 3] * sc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV
+// ---------------------------------------------------------------------------
+template <typename T, typename G, int D, int BR, bool DROP>
+__global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnArgs a) {
+  using S = TileShape<T, D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr int KI = M::KI, KH = M::KH;
+  constexpr int BK = 128;  // keys per workgroup
+  constexpr int NQB = BR / 32, NDB = D / 32, NC = D / KI;
+  constexpr int NLD = BR * S::KCH / 256;
+  constexpr int TILE = BR * S::KS;
+  static_assert((BR * S::KCH) % 256 == 0 && BR <= 256 && BK % BR == 0, "tile shape");
+  constexpr float NEG_INF = -__builtin_inff(), POS_INF = __builtin_inff();
+
+  __shared__ __attribute__((aligned(16))) T smem[2][2 * TILE];  // [buffer][Q tile | dO tile]
+  __shared__ __attribute__((aligned(16))) float side_l[2][BR];  // LSE in log2 units (+inf: no valid key)
+  __shared__ __attribute__((aligned(16))) float side_d[2][BR];  // D_i
+  __shared__ __attribute__((aligned(16))) uint32_t side_h[2][BR];  // dropout row hash
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lo = lane & 31, hi = lane >> 5;
+  const int N = a.N;
+  const int rank = blockIdx.x / a.BH;
+  const int bh = blockIdx.x - rank * a.BH;
+  const int kt = rank;  // causal: low key tiles see the most query rows, so they go first
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const T* __restrict__ Qg = static_cast<const T*>(a.q) + hoff;
+  const T* __restrict__ Kg = static_cast<const T*>(a.k) + hoff;
+  const T* __restrict__ Vg = static_cast<const T*>(a.v) + hoff;
+  const T* __restrict__ dOg = static_cast<const T*>(a.dout) + hoff;
+  const float* __restrict__ Lg = a.lse + (size_t)bh * N;
+  const float* __restrict__ Dg = a.delta + (size_t)bh * N;
+  G* __restrict__ dKg = static_cast<G*>(a.dk) + hoff;
+  G* __restrict__ dVg = static_cast<G*>(a.dv) + hoff;
+
+  const int k0wg = kt * BK;
+  const int k0w = k0wg + w * 32;
+  const int key = k0w + lo;
+  const bool kvalid = key < N;
+
+  frag kf[NC], vf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int off = key * D + c * KI + hi * KH;
+    kf[c] = kvalid ? load_frag<T>(Kg + off) : zero_frag<T>();
+    vf[c] = kvalid ? load_frag<T>(Vg + off) : zero_frag<T>();
+  }
+  uint32_t hk = 0;
+  if constexpr (DROP) hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
+
+  // Query tiles this workgroup visits: causal starts at its diagonal; a
+  // block mask skips query tiles whose (row block, this column block) is empty.
+  const int nqt = (N + BR - 1) / BR;
+  const int istart = a.causal ? (k0wg / BR) : 0;
+  const int cblk = k0wg / a.mask_block;
+  auto kept = [&](int i) {
+    return a.bmask == nullptr || a.bmask[(size_t)((i * BR) / a.mask_block) * a.nb + cblk] != 0;
+  };
+  auto next_kept = [&](int i) {
+    ++i;
+    while (i < nqt && !kept(i)) ++i;
+    return i;
+  };
+
+  u32x4 qreg[NLD], oreg[NLD];
+  float l_reg = POS_INF, d_reg = 0.f;
+  uint32_t h_reg = 0;
+  auto gload = [&](int it) {
+    const int i0 = it * BR;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = i * 256 + tid;
+      const int row = c / S::KCH, ch = c % S::KCH;
+      const int qi = i0 + row;
+      const size_t off = (size_t)qi * D + ch * S::EPC;
+      qreg[i] = qi < N ? *reinterpret_cast<const u32x4*>(Qg + off) : u32x4{0, 0, 0, 0};
+      oreg[i] = qi < N ? *reinterpret_cast<const u32x4*>(dOg + off) : u32x4{0, 0, 0, 0};
+    }
+    if (tid < BR) {
+      const int qi = i0 + tid;
+      l_reg = POS_INF;
+      d_reg = 0.f;
+      if (qi < N) {
+        const float l = Lg[qi];
+        l_reg = (l == NEG_INF) ? POS_INF : l * kLog2e;
+        d_reg = Dg[qi];
+      }
+      if constexpr (DROP) h_reg = fmix32(hk ^ (uint32_t)qi);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = i * 256 + tid;
+      const int row = c / S::KCH, ch = c % S::KCH;
+      *reinterpret_cast<u32x4*>(&smem[buf][row * S::KS + ch * S::EPC]) = qreg[i];
+      *reinterpret_cast<u32x4*>(&smem[buf][TILE + row * S::KS + ch * S::EPC]) = oreg[i];
+    }
+    if (tid < BR) {
+      side_l[buf][tid] = l_reg;
+      side_d[buf][tid] = d_reg;
+      side_h[buf][tid] = h_reg;
+    }
+  };
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+
+  int it = istart < nqt && kept(istart) ? istart : next_kept(istart);
+  int cur = 0;
+  if (it < nqt) {
+    gload(it);
+    sstore(0);
+  }
+  __syncthreads();
+
+  while (it < nqt) {
+    const int itn = next_kept(it);
+    if (itn < nqt) gload(itn);
+    const T* Qs = &smem[cur][0];
+    const T* dOs = &smem[cur][TILE];
+    const int i0 = it * BR;
+    // The wave has work unless every query of the tile is above its keys.
+    const bool active = (k0w < N) && (!a.causal || i0 + BR - 1 >= k0w);
+    if (active) {
+      f32x16 s[NQB], dp[NQB];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        s[qb] = zero16();
+        dp[qb] = zero16();
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const int off = (qb * 32 + lo) * S::KS + c * KI + hi * KH;
+          s[qb] = M::run(load_frag<T>(Qs + off), kf[c], s[qb]);
+          dp[qb] = M::run(load_frag<T>(dOs + off), vf[c], dp[qb]);
+        }
+      const bool need_mask = (a.causal && i0 < k0w + 31) || (k0w + 31 >= N);
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int qi = i0 + qb * 32 + crow(v, hi);
+            if (!kvalid || (a.causal && key > qi)) s[qb][v] = NEG_INF;
+          }
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ql = qb * 32 + 8 * g + 4 * hi;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&side_l[cur][ql]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&side_d[cur][ql]);
+          u32x4 h4 = {0, 0, 0, 0};
+          if constexpr (DROP) h4 = *reinterpret_cast<const u32x4*>(&side_h[cur][ql]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * g + e;
+            const float p = exp2_fast(fmaf(s[qb][v], a.sl2, -l4[e]));
+            float pd = p, dpv = dp[qb][v];
+            if constexpr (DROP) {
+              const bool keep = fmix32(h4[e] ^ (uint32_t)key) >= a.thresh;
+              pd = keep ? p * a.rp : 0.f;
+              dpv = keep ? dpv * a.rp : 0.f;
+            }
+            s[qb][v] = pd;                    // P * Z / (1 - p)
+            dp[qb][v] = p * (dpv - d4[e]);    // dS
+          }
+        }
+      if constexpr (KH == 8) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const frag bp = pack8<T>(s[qb][8 * hf + 0], s[qb][8 * hf + 1], s[qb][8 * hf + 2], s[qb][8 * hf + 3],
+                                     s[qb][8 * hf + 4], s[qb][8 * hf + 5], s[qb][8 * hf + 6], s[qb][8 * hf + 7]);
+            const frag bs = pack8<T>(dp[qb][8 * hf + 0], dp[qb][8 * hf + 1], dp[qb][8 * hf + 2], dp[qb][8 * hf + 3],
+                                     dp[qb][8 * hf + 4], dp[qb][8 * hf + 5], dp[qb][8 * hf + 6], dp[qb][8 * hf + 7]);
+            const int base = qb * 32 + 16 * hf;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              dv[db] = M::run(load_frag_tr<T>(dOs, S::KS, base, db * 32, lane), bp, dv[db]);
+              dk[db] = M::run(load_frag_tr<T>(Qs, S::KS, base, db * 32, lane), bs, dk[db]);
+            }
+          }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int ql = qb * 32 + crow(v, hi);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              dv[db] = M::run(dOs[ql * S::KS + db * 32 + lo], s[qb][v], dv[db]);
+              dk[db] = M::run(Qs[ql * S::KS + db * 32 + lo], dp[qb][v], dk[db]);
+            }
+          }
+      }
+    }
+    if (itn < nqt) sstore(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+    it = itn;
+  }
+
+  if (kvalid) {
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int off = key * D + db * 32 + 8 * g + 4 * hi;
+        store4<G>(dKg + off, dk[db][4 * g] * sc, dk[db][4 * g + 1] * sc, dk[db][4 * g + 2] * sc,
+                  dk[db][4 * g + 3] * sc);
+        store4<G>(dVg + off, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+template <typename T, typename G, int D, int BC, int BR, bool DROP>
+static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t s) {
+  const int nq = (a.N + 127) / 128;
+  bwd_dq_kernel<T, G, D, BC, DROP><<<dim3((unsigned)(nq * a.BH)), dim3(256), 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_dkdv_kernel<T, G, D, BR, DROP><<<dim3((unsigned)(nq * a.BH)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, typename G, int D, int BC, int BR>
+static hipError_t launch_bwd_d(bool dropout, const AttnArgs& a, hipStream_t s) {
+  return dropout ? launch_bwd_t<T, G, D, BC, BR, true>(a, s) : launch_bwd_t<T, G, D, BC, BR, false>(a, s);
+}
+
+template <typename T>
+static hipError_t launch_bwd_16(bool f32grad, int d, bool dropout, const AttnArgs& a, hipStream_t s) {
+  if (f32grad)
+    return d == 64 ? launch_bwd_d<T, float, 64, 64, 64>(dropout, a, s)
+                   : launch_bwd_d<T, float, 128, 64, 64>(dropout, a, s);
+  return d == 64 ? launch_bwd_d<T, T, 64, 64, 64>(dropout, a, s) : launch_bwd_d<T, T, 128, 64, 64>(dropout, a, s);
+}
+
+hipError_t launch_bwd(Elt t, Elt gt, int d, bool dropout, const AttnArgs& a, hipStream_t s) {
+  switch (t) {
+    case Elt::BF16:
+      return launch_bwd_16<__bf16>(gt == Elt::F32, d, dropout, a, s);
+    case Elt::F16:
+      return launch_bwd_16<_Float16>(gt == Elt::F32, d, dropout, a, s);
+    case Elt::F32:
+      return d == 64 ? launch_bwd_d<float, float, 64, 64, 64>(dropout, a, s)
+                     : launch_bwd_d<float, float, 128, 32, 32>(dropout, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,177 @@
+// Device-side building blocks for the gfx950 attention kernels: MFMA
+// wrappers, operand fragments, type conversion and the dropout hash.
+//
+// MFMA operand layout used throughout (32x32 output tiles, wave64):
+//   A (32 x KI): lane l holds row (l % 32), k elements [KH*(l/32), KH*(l/32)+KH)
+//   B (KI x 32): lane l holds column (l % 32), the same k elements
+//   C (32 x 32): lane l holds column (l % 32), rows 8*(v/4) + 4*(l/32) + (v%4)
+//                for accumulator element v = 0..15
+// KI = 16, KH = 8 for bf16/fp16 (v_mfma_f32_32x32x16_{bf16,f16});
+// KI = 2,  KH = 1 for fp32      (v_mfma_f32_32x32x2_f32).
+// Only the A/B row/column mapping and the C layout matter for results:
+// A and B are always filled with the same k order, so the sum over k is the
+// same whatever the hardware's internal k order is.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<__bf16> {
+  using frag = bf16x8;
+  using half = bf16x4;
+  static constexpr int KI = 16, KH = 8;
+  static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<_Float16> {
+  using frag = f16x8;
+  using half = f16x4;
+  static constexpr int KI = 16, KH = 8;
+  static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  using frag = float;
+  using half = float;
+  static constexpr int KI = 2, KH = 1;
+  static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// KH contiguous elements starting at p (16-byte aligned for 16-bit types).
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag load_frag(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(typename Mfma<T>::frag, *reinterpret_cast<const u32x4*>(p));
+  } else {
+    return *p;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag zero_frag() {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(typename Mfma<T>::frag, u32x4{0u, 0u, 0u, 0u});
+  } else {
+    return 0.f;
+  }
+}
+
+// Two groups of 4 contiguous 16-bit elements (8-byte aligned) joined into
+// one 8-element fragment.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag load_frag_2x4(const T* p0, const T* p1) {
+  static_assert(sizeof(T) == 2, "16-bit only");
+  u32x2 a = *reinterpret_cast<const u32x2*>(p0);
+  u32x2 b = *reinterpret_cast<const u32x2*>(p1);
+  return __builtin_bit_cast(typename Mfma<T>::frag, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return static_cast<T>(x); }
+
+// Eight fp32 values -> one 16-bit fragment (round to nearest even).
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag pack8(float x0, float x1, float x2, float x3,
+                                                          float x4, float x5, float x6, float x7) {
+  typename Mfma<T>::frag f;
+  f[0] = static_cast<T>(x0); f[1] = static_cast<T>(x1);
+  f[2] = static_cast<T>(x2); f[3] = static_cast<T>(x3);
+  f[4] = static_cast<T>(x4); f[5] = static_cast<T>(x5);
+  f[6] = static_cast<T>(x6); f[7] = static_cast<T>(x7);
+  return f;
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Exchange with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// MurmurHash3 32-bit finalizer (Appleby, public domain).
+__device__ __forceinline__ uint32_t fmix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  x *= 0xC2B2AE35u;
+  x ^= x >> 16;
+  return x;
+}
+
+// Per-(b, h) dropout key from the 64-bit seed.
+__device__ __forceinline__ uint32_t head_key(uint32_t seed_lo, uint32_t seed_hi, uint32_t b, uint32_t h) {
+  uint32_t k = fmix32(seed_lo + 0x9E3779B9u);
+  k = fmix32(k ^ seed_hi);
+  k = fmix32(k ^ b);
+  return fmix32(k ^ h);
+}
+
+// Key index of accumulator element v in a 32x32 C tile whose rows are keys.
+__device__ __forceinline__ int crow(int v, int hi) { return 8 * (v >> 2) + 4 * hi + (v & 3); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// A-operand fragment built from the COLUMNS of a row-major 16-bit LDS tile
+// (element (r, c) at tile[r * stride + c]): lane l receives column
+// col0 + (l % 32) and the tile rows base + 4*(l/32) + {0,1,2,3} followed by
+// base + 8 + 4*(l/32) + {0,1,2,3}, i.e. the same k order as elements
+// 8*hf .. 8*hf+7 of a 32x32 accumulator tile (crow) when base = 32*kb + 16*hf.
+// Uses the gfx950 LDS transpose read (ds_read_b64_tr_b16): within each group
+// of 16 lanes, lane j's element e is element (j % 4) of the 8 bytes addressed
+// by lane 4*e + j/4 of the group. `stride` and col0 must be multiples of 4.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag load_frag_tr(const T* tile, int stride, int base, int col0,
+                                                                int lane) {
+  static_assert(sizeof(T) == 2, "16-bit only");
+  const int j = lane & 15;
+  const T* p = tile + (base + 4 * (lane >> 5) + (j >> 2)) * stride + col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * stride));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 xy = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(typename Mfma<T>::frag, xy);
+}
+
+// Stores 4 consecutive fp32 values as type G (one vector store).
+template <typename G>
+__device__ __forceinline__ void store4(G* p, float x0, float x1, float x2, float x3) {
+  typedef G g4 __attribute__((ext_vector_type(4)));
+  g4 r;
+  r[0] = static_cast<G>(x0);
+  r[1] = static_cast<G>(x1);
+  r[2] = static_cast<G>(x2);
+  r[3] = static_cast<G>(x3);
+  *reinterpret_cast<g4*>(p) = r;
+}
+
+}  // namespace fa
