@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Throughput of tiled exact attention (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+fa_fwd (O, LSE), then the two backward stages fa_bwd_dq (D, dQ) and
+fa_bwd_dkdv (dK, dV), all through the C ABI on the current HIP stream.
+Inputs are resident in device memory before the timed region. The default
+workload is the GPT-2-medium attention layer (B=8, H=16, N=1024, d=64, bf16,
+causal). Prints ONE JSON line on stdout; per-kernel detail goes to stderr.
+
+FLOP convention: forward 4*B*H*N^2*d (halved when causal, kept-block count
+when block-sparse), backward 2.5x forward.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s and % MFMA peak on 1 MI355X (bf16, N=1k–16k)"
+# Published MI355X peaks: dense MFMA (TFLOP/s) by operand type, HBM3E (GB/s).
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+DTYPE_NAME = {"bf16": "bf16", "fp16": "fp16", "fp32": "fp32"}
+
+WORKLOAD_TEXT = {
+    "C1": "single-head attention forward, fp32: B=1 H=1 N=128 d=64, non-causal",
+    "C2": "GPT-2-medium attention layer fwd+bwd: B=8 H=16 N=1024 d=64 bf16 causal",
+    "C3": "training-style attention fwd+bwd: B=4 H=16 N=4096 d=64 bf16 causal dropout 0.1",
+    "C4": "long-context attention fwd+bwd: B=1 H=32 N=16384 d=128 bf16 causal, K x2",
+    "C5": "block-sparse attention fwd+bwd: B=2 H=16 N=8192 d=64 bf16, 128x128 blocks (518/4096 kept)",
+}
+
+
+def src_digest() -> str:
+    """sha256 over the kernel sources and the ABI header (ties profiles to code)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "io_aware_exact_14_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "fa.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def convention_flops(w, kept_blocks):
+    B, H, N, d = w.B, w.H, w.N, w.d
+    if w.block_sparse:
+        fwd = 4.0 * B * H * d * w.mask_block ** 2 * kept_blocks
+    else:
+        fwd = 4.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
+    return fwd, (2.5 * fwd if w.backward else 0.0)
+
+
+def kernel_model(w, kept_blocks, el_bytes, grad_bytes):
+    """Algorithmic flops and compulsory bytes per launch of each kernel.
+
+    Flops: 2*d per visible (query, key) pair per matrix product the kernel's
+    outputs require (forward 2: QK^T, PV; dQ 3: QK^T, dO V^T, dS K; dK/dV 4:
+    QK^T, dO V^T, P^T dO, dS^T Q). Bytes: each tensor the kernel must read or
+    write once (Q, K, V, O, dO, gradients, LSE and D rows)."""
+    B, H, N, d = w.B, w.H, w.N, w.d
+    if w.block_sparse:
+        pairs = B * H * w.mask_block ** 2 * kept_blocks
+    else:
+        pairs = B * H * N * N * (0.5 if w.causal else 1.0)
+    t = B * H * N * d  # elements of one [B][H][N][d] tensor
+    rows = B * H * N
+    m = {"fwd_kernel": (2 * 2 * d * pairs, 3 * t * el_bytes + t * el_bytes + 4 * rows)}
+    if w.backward:
+        m["bwd_dq_kernel"] = (3 * 2 * d * pairs, 5 * t * el_bytes + 4 * rows + t * grad_bytes + 4 * rows)
+        m["bwd_dkdv_kernel"] = (4 * 2 * d * pairs, 4 * t * el_bytes + 8 * rows + 2 * t * grad_bytes)
+    return m
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("src_sha256") != src_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x, target_s=12.0):
+    """The fp64 oracle, as it stands, timed on the host over a bounded sample
+    of the workload's heads (forward + backward per head)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    bm = x["block_mask"]
+    done, t0 = 0, time.perf_counter()
+    for (b, h) in heads:
+        oracle.forward_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], w.scale, w.causal, w.dropout_p,
+                            w.dropout_seed, b, h, bm, w.mask_block)
+        if w.backward:
+            oracle.backward_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["do"][b, h], w.scale, w.causal,
+                                 w.dropout_p, w.dropout_seed, b, h, bm, w.mask_block)
+        done += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    kept = int(np.asarray(bm).sum()) if bm is not None else 0
+    f, bwd = convention_flops(w, kept)
+    per_head = (f + bwd) / (w.B * w.H)
+    return {
+        "value": round(per_head * done / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.H} (b,h) heads of the same workload, fp64 numpy forward+backward "
+                  f"per head, {dt:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="C2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 512 MiB device copy first (reference kernel for HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the attention path here is single-GPU "
+              "(heads would shard over GPUs with no communication); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import io_aware_exact_14_amd as fa
+    from io_aware_exact_14_amd import _lib
+    from workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    x = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    do = x["do"].to(dev) if w.backward else None
+    bm = x["block_mask"]
+    kept = int(np.asarray(bm).sum()) if bm is not None else 0
+    bm_dev = torch.from_numpy(bm).to(dev) if bm is not None else None
+    grad_dtype = torch.float32
+    p = fa.params(w.B, w.H, w.N, w.d, w.torch_dtype, grad_dtype=grad_dtype, scale=w.scale, causal=w.causal,
+                  dropout_p=w.dropout_p, seed=w.dropout_seed, block_mask=bm_dev, mask_block=w.mask_block)
+    lib = _lib.load()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    if w.backward:
+        dq, dk, dv = (torch.empty(q.shape, dtype=grad_dtype, device=dev) for _ in range(3))
+        ws_n = int(lib.fa_bwd_workspace_bytes(ctypes.byref(p)))
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+    if args.copy_calibration:
+        src = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    pp = ctypes.byref(p)
+    fwd_args = (pp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), sp)
+    if w.backward:
+        dq_args = (pp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                   dq.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+        dkdv_args = (pp, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(), dk.data_ptr(),
+                     dv.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+    names = ["fwd_kernel"] + (["bwd_dq_kernel", "bwd_dkdv_kernel"] if w.backward else [])
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        st = lib.fa_fwd(*fwd_args)
+        if ev is not None:
+            ev[1].record(stream)
+        if w.backward:
+            st |= lib.fa_bwd_dq(*dq_args)
+            if ev is not None:
+                ev[2].record(stream)
+            st |= lib.fa_bwd_dkdv(*dkdv_args)
+            if ev is not None:
+                ev[3].record(stream)
+        if st != 0:
+            raise RuntimeError(f"libfa returned status {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    kdur = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
+    f_fwd, f_bwd = convention_flops(w, kept)
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+
+    el = torch.tensor([], dtype=w.torch_dtype).element_size()
+    model = kernel_model(w, kept, el, torch.tensor([], dtype=grad_dtype).element_size())
+    dom = max(names, key=lambda n: kdur[n])
+    flops_k, bytes_k = model[dom]
+    peak_f = PEAK_TFLOPS[w.dtype]
+    t_mfma = flops_k / (peak_f * 1e12)
+    t_hbm = bytes_k / (PEAK_HBM_GBS * 1e9)
+    sec = kdur[dom] * 1e-3
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": round(flops_k / sec / 1e12, 3), "peak": peak_f, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(bytes_k / sec / 1e9, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 5)
+    roof["kernel"] = dom
+    roof["traffic"] = read_traffic(dom, w.name)
+
+    detail = {n: {"avg_ms": round(kdur[n], 5), "tflops": round(model[n][0] / (kdur[n] * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(model[n][0] / (kdur[n] * 1e-3) / (peak_f * 1e12), 4),
+                  "gbs": round(model[n][1] / (kdur[n] * 1e-3) / 1e9, 1)} for n in names}
+    print(json.dumps({"per_kernel": detail, "fwd_tflops": round(f_fwd / (kdur["fwd_kernel"] * 1e-3) / 1e12, 2),
+                      "bwd_tflops": round(f_bwd / (sum(kdur[n] for n in names[1:]) * 1e-3) / 1e12, 2)
+                      if w.backward else None}), file=sys.stderr, flush=True)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {WORKLOAD_TEXT[w.name]}", "global_batch": w.B, "heads": w.H,
+                   "seq_len": w.N, "head_dim": w.d, "grad_dtype": "fp32", "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

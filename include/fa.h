@@ -116,6 +116,21 @@ int fa_bwd(const fa_params* p, const void* Q, const void* K, const void* V,
            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two stages of fa_bwd, for callers that time or schedule them apart.
+ * fa_bwd_dq computes D_i = dO_i . O_i into `workspace` and writes dQ;
+ * fa_bwd_dkdv reads D from the same workspace and writes dK and dV, so it
+ * must be enqueued after fa_bwd_dq (same stream, or an event between them)
+ * with the same parameters, inputs and workspace. fa_bwd == fa_bwd_dq
+ * followed by fa_bwd_dkdv on one stream.
+ */
+int fa_bwd_dq(const fa_params* p, const void* Q, const void* K, const void* V,
+              const void* O, const float* LSE, const void* dO, void* dQ,
+              void* workspace, size_t workspace_bytes, void* stream);
+int fa_bwd_dkdv(const fa_params* p, const void* Q, const void* K, const void* V,
+                const float* LSE, const void* dO, void* dK, void* dV,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Writes the dropout keep bits Z_ij (1 = kept) of head (b, h) for query rows
  * [i0, i0+rows) and key columns [j0, j0+cols) into the DEVICE buffer
  * keep[rows][cols], with the same device function the fused kernels use.

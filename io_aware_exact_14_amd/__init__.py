@@ -22,7 +22,8 @@ from ._lib import FA_BF16, FA_F16, FA_F32, FaParams, STATUS_NAMES
 
 _lib.load()
 
-__all__ = ["forward", "backward", "dropout_mask", "bwd_workspace_bytes", "FaError", "params"]
+__all__ = ["forward", "backward", "backward_dq", "backward_dkdv", "dropout_mask", "bwd_workspace_bytes",
+           "FaError", "params"]
 
 _DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
@@ -107,11 +108,9 @@ def bwd_workspace_bytes(B, H, N, d, dtype=torch.bfloat16, **kw) -> int:
     return int(_lib.load().fa_bwd_workspace_bytes(ctypes.byref(p)))
 
 
-def backward(q, k, v, o, lse, do, *, scale=None, causal=False, dropout_p=0.0, seed=0, block_mask=None,
-             mask_block=128, grad_dtype=torch.float32, workspace=None, dq=None, dk=None, dv=None):
-    """dQ, dK, dV of exact attention (recomputes S and P from q, k and lse)."""
+def _bwd_setup(q, k, v, o, lse, do, scale, causal, dropout_p, seed, block_mask, mask_block, grad_dtype, workspace):
     B, H, N, d = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)) + ((("o", o),) if o is not None else ()):
         _require(t, name, (B, H, N, d), q.dtype)
     _require(lse, "lse", (B, H, N), torch.float32)
     bm = _mask_arg(block_mask, N, mask_block, q.device)
@@ -121,16 +120,52 @@ def backward(q, k, v, o, lse, do, *, scale=None, causal=False, dropout_p=0.0, se
     need = int(lib.fa_bwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    grads = []
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t is None:
-            t = torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device)
-        _require(t, name, (B, H, N, d), grad_dtype)
-        grads.append(t)
+    return p, bm, lib, workspace
+
+
+def _grad(t, name, shape, grad_dtype, device):
+    if t is None:
+        t = torch.empty(shape, dtype=grad_dtype, device=device)
+    _require(t, name, shape, grad_dtype)
+    return t
+
+
+def _ws(workspace):
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def backward(q, k, v, o, lse, do, *, scale=None, causal=False, dropout_p=0.0, seed=0, block_mask=None,
+             mask_block=128, grad_dtype=torch.float32, workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV of exact attention (recomputes S and P from q, k and lse)."""
+    p, bm, lib, workspace = _bwd_setup(q, k, v, o, lse, do, scale, causal, dropout_p, seed, block_mask,
+                                       mask_block, grad_dtype, workspace)
+    dq, dk, dv = (_grad(t, n, q.shape, grad_dtype, q.device) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
     _check(lib.fa_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                      do.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
-                      workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()), "fa_bwd")
-    return tuple(grads)
+                      do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *_ws(workspace), _stream()),
+           "fa_bwd")
+    return dq, dk, dv
+
+
+def backward_dq(q, k, v, o, lse, do, *, workspace, scale=None, causal=False, dropout_p=0.0, seed=0,
+                block_mask=None, mask_block=128, grad_dtype=torch.float32, dq=None):
+    """First backward stage: D_i = dO_i . O_i into ``workspace``, and dQ."""
+    p, bm, lib, workspace = _bwd_setup(q, k, v, o, lse, do, scale, causal, dropout_p, seed, block_mask,
+                                       mask_block, grad_dtype, workspace)
+    dq = _grad(dq, "dq", q.shape, grad_dtype, q.device)
+    _check(lib.fa_bwd_dq(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         do.data_ptr(), dq.data_ptr(), *_ws(workspace), _stream()), "fa_bwd_dq")
+    return dq
+
+
+def backward_dkdv(q, k, v, lse, do, *, workspace, scale=None, causal=False, dropout_p=0.0, seed=0,
+                  block_mask=None, mask_block=128, grad_dtype=torch.float32, dk=None, dv=None):
+    """Second backward stage (after backward_dq with the same workspace): dK, dV."""
+    p, bm, lib, workspace = _bwd_setup(q, k, v, None, lse, do, scale, causal, dropout_p, seed, block_mask,
+                                       mask_block, grad_dtype, workspace)
+    dk, dv = (_grad(t, n, q.shape, grad_dtype, q.device) for t, n in ((dk, "dk"), (dv, "dv")))
+    _check(lib.fa_bwd_dkdv(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), dk.data_ptr(), dv.data_ptr(), *_ws(workspace), _stream()), "fa_bwd_dkdv")
+    return dk, dv
 
 
 def dropout_mask(B, H, N, d, b, h, i0, rows, j0, cols, *, dropout_p, seed, dtype=torch.bfloat16,

@@ -34,6 +34,8 @@ EXPORTS = (
     "fa_fwd",
     "fa_bwd_workspace_bytes",
     "fa_bwd",
+    "fa_bwd_dq",
+    "fa_bwd_dkdv",
     "fa_dropout_mask",
 )
 
@@ -70,6 +72,10 @@ def _declare(lib):
     lib.fa_bwd_workspace_bytes.argtypes = [P]
     lib.fa_bwd.restype = i32
     lib.fa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_dq.restype = i32
+    lib.fa_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_dkdv.restype = i32
+    lib.fa_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fa_dropout_mask.restype = i32
     lib.fa_dropout_mask.argtypes = [P, i64, i64, i64, i64, i64, i64, vp, vp]
     return lib
@@ -84,7 +90,7 @@ def load():
     global _LIB
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
-            raise OSError(f"{LIB_PATH} is missing: build it with `python -m io_aware_exact_14_amd.build`")
+            raise OSError(f"{LIB_PATH} is missing: build it with `python io_aware_exact_14_amd/build.py`")
         lib = _declare(ctypes.CDLL(LIB_PATH))
         if lib.fa_abi_version() != ABI_VERSION:
             raise OSError(f"libfa ABI version {lib.fa_abi_version()} != {ABI_VERSION}")

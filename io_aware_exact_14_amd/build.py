@@ -1,6 +1,8 @@
 """Builds libfa.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m io_aware_exact_14_amd.build [--verbose] [--resource-usage]
+    python io_aware_exact_14_amd/build.py [--verbose] [--resource-usage]
+
+It never imports the package (whose import loads the library).
 
 Every .hip file under csrc/ is compiled to an object with hipcc, in
 parallel, then linked into io_aware_exact_14_amd/libfa.so. Packed fp32 VALU

@@ -101,14 +101,21 @@ size_t fa_bwd_workspace_bytes(const fa_params* p) {
   return (rows * sizeof(float) + 255) / 256 * 256;
 }
 
-int fa_bwd(const fa_params* p, const void* Q, const void* K, const void* V, const void* O, const float* LSE,
-           const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared validation and launch of the backward stages (stage bit 1: dQ and D,
+// bit 2: dK and dV). Pointers a stage does not touch may be NULL.
+int bwd_stage(int stage, const fa_params* p, const void* Q, const void* K, const void* V, const void* O,
+              const float* LSE, const void* dO, void* dQ, void* dK, void* dV, void* workspace,
+              size_t workspace_bytes, void* stream) {
   const int st = check(p);
   if (st != FA_OK) return st;
-  if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV) return FA_ERR_NULL;
+  if (!Q || !K || !V || !LSE || !dO) return FA_ERR_NULL;
+  if ((stage & 1) && (!O || !dQ)) return FA_ERR_NULL;
+  if ((stage & 2) && (!dK || !dV)) return FA_ERR_NULL;
   const void* ptrs[] = {Q, K, V, O, LSE, dO, dQ, dK, dV};
   for (const void* x : ptrs)
-    if (!aligned16(x)) return FA_ERR_ALIGN;
+    if (x != nullptr && !aligned16(x)) return FA_ERR_ALIGN;
   const size_t need = fa_bwd_workspace_bytes(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
   if (workspace != nullptr && !aligned16(workspace)) return FA_ERR_ALIGN;
@@ -124,9 +131,27 @@ int fa_bwd(const fa_params* p, const void* Q, const void* K, const void* V, cons
   a.dk = dK;
   a.dv = dV;
   a.delta = static_cast<float*>(workspace);
-  const hipError_t e = fa::launch_bwd(elt(p->in_dtype), elt(p->grad_dtype), (int)p->d, a.thresh != 0, a,
+  const hipError_t e = fa::launch_bwd(elt(p->in_dtype), elt(p->grad_dtype), (int)p->d, a.thresh != 0, stage, a,
                                       (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+int fa_bwd(const fa_params* p, const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+           const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dK || !dV) return FA_ERR_NULL;  // all three gradients are required here
+  return bwd_stage(3, p, Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_dq(const fa_params* p, const void* Q, const void* K, const void* V, const void* O, const float* LSE,
+              const void* dO, void* dQ, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_stage(1, p, Q, K, V, O, LSE, dO, dQ, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_dkdv(const fa_params* p, const void* Q, const void* K, const void* V, const float* LSE, const void* dO,
+                void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_stage(2, p, Q, K, V, nullptr, LSE, dO, nullptr, dK, dV, workspace, workspace_bytes, stream);
 }
 
 int fa_dropout_mask(const fa_params* p, int64_t b, int64_t h, int64_t i0, int64_t rows, int64_t j0, int64_t cols,

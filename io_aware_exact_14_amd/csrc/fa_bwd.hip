@@ -463,37 +463,44 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnArgs a) {
 // launch
 // ---------------------------------------------------------------------------
 template <typename T, typename G, int D, int BC, int BR, bool DROP>
-static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t s) {
-  const int nq = (a.N + 127) / 128;
-  bwd_dq_kernel<T, G, D, BC, DROP><<<dim3((unsigned)(nq * a.BH)), dim3(256), 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  bwd_dkdv_kernel<T, G, D, BR, DROP><<<dim3((unsigned)(nq * a.BH)), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
+static hipError_t launch_bwd_t(int stage, const AttnArgs& a, hipStream_t s) {
+  const int nt = (a.N + 127) / 128;  // 128-row query tiles (dQ) and 128-row key tiles (dK/dV)
+  if (stage & 1) {
+    bwd_dq_kernel<T, G, D, BC, DROP><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stage & 2) {
+    bwd_dkdv_kernel<T, G, D, BR, DROP><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <typename T, typename G, int D, int BC, int BR>
-static hipError_t launch_bwd_d(bool dropout, const AttnArgs& a, hipStream_t s) {
-  return dropout ? launch_bwd_t<T, G, D, BC, BR, true>(a, s) : launch_bwd_t<T, G, D, BC, BR, false>(a, s);
+static hipError_t launch_bwd_d(bool dropout, int stage, const AttnArgs& a, hipStream_t s) {
+  return dropout ? launch_bwd_t<T, G, D, BC, BR, true>(stage, a, s)
+                 : launch_bwd_t<T, G, D, BC, BR, false>(stage, a, s);
 }
 
 template <typename T>
-static hipError_t launch_bwd_16(bool f32grad, int d, bool dropout, const AttnArgs& a, hipStream_t s) {
+static hipError_t launch_bwd_16(bool f32grad, int d, bool dropout, int stage, const AttnArgs& a, hipStream_t s) {
   if (f32grad)
-    return d == 64 ? launch_bwd_d<T, float, 64, 64, 64>(dropout, a, s)
-                   : launch_bwd_d<T, float, 128, 64, 64>(dropout, a, s);
-  return d == 64 ? launch_bwd_d<T, T, 64, 64, 64>(dropout, a, s) : launch_bwd_d<T, T, 128, 64, 64>(dropout, a, s);
+    return d == 64 ? launch_bwd_d<T, float, 64, 64, 64>(dropout, stage, a, s)
+                   : launch_bwd_d<T, float, 128, 64, 64>(dropout, stage, a, s);
+  return d == 64 ? launch_bwd_d<T, T, 64, 64, 64>(dropout, stage, a, s)
+                 : launch_bwd_d<T, T, 128, 64, 64>(dropout, stage, a, s);
 }
 
-hipError_t launch_bwd(Elt t, Elt gt, int d, bool dropout, const AttnArgs& a, hipStream_t s) {
+hipError_t launch_bwd(Elt t, Elt gt, int d, bool dropout, int stage, const AttnArgs& a, hipStream_t s) {
   switch (t) {
     case Elt::BF16:
-      return launch_bwd_16<__bf16>(gt == Elt::F32, d, dropout, a, s);
+      return launch_bwd_16<__bf16>(gt == Elt::F32, d, dropout, stage, a, s);
     case Elt::F16:
-      return launch_bwd_16<_Float16>(gt == Elt::F32, d, dropout, a, s);
+      return launch_bwd_16<_Float16>(gt == Elt::F32, d, dropout, stage, a, s);
     case Elt::F32:
-      return d == 64 ? launch_bwd_d<float, float, 64, 64, 64>(dropout, a, s)
-                     : launch_bwd_d<float, float, 128, 32, 32>(dropout, a, s);
+      return d == 64 ? launch_bwd_d<float, float, 64, 64, 64>(dropout, stage, a, s)
+                     : launch_bwd_d<float, float, 128, 32, 32>(dropout, stage, a, s);
   }
   return hipErrorInvalidValue;
 }

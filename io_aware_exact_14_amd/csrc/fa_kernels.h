@@ -39,7 +39,8 @@ struct AttnArgs {
 };
 
 hipError_t launch_fwd(Elt t, int d, bool dropout, const AttnArgs& a, hipStream_t s);
-hipError_t launch_bwd(Elt t, Elt gt, int d, bool dropout, const AttnArgs& a, hipStream_t s);
+// stage: 1 = dQ (and D), 2 = dK/dV, 3 = both in order
+hipError_t launch_bwd(Elt t, Elt gt, int d, bool dropout, int stage, const AttnArgs& a, hipStream_t s);
 hipError_t launch_dropout_mask(const AttnArgs& a, int b, int h, int64_t i0, int64_t rows, int64_t j0,
                                int64_t cols, uint8_t* keep, hipStream_t s);
 

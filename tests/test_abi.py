@@ -10,19 +10,29 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _ensure_built():
+    lib_path = os.path.join(ROOT, "io_aware_exact_14_amd", "libfa.so")
+    if not os.path.exists(lib_path):
+        import importlib.util
+
+        spec = importlib.util.spec_from_file_location("_fa_build", os.path.join(ROOT, "io_aware_exact_14_amd",
+                                                                               "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+
+
 @pytest.fixture(scope="module")
 def lib():
+    _ensure_built()
     from io_aware_exact_14_amd import _lib
 
-    if not os.path.exists(_lib.LIB_PATH):
-        from io_aware_exact_14_amd import build
-
-        build.build()
     return _lib.load()
 
 
 @pytest.fixture(scope="module")
 def L():
+    _ensure_built()
     from io_aware_exact_14_amd import _lib
 
     return _lib
@@ -102,6 +112,8 @@ def test_invalid_params_rejected(lib, L, kw, status):
     dummy = 4096
     assert lib.fa_fwd(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, None) == L.STATUS[status]
     assert lib.fa_bwd(ctypes.byref(p), *([dummy] * 9), dummy, 1 << 30, None) == L.STATUS[status]
+    assert lib.fa_bwd_dq(ctypes.byref(p), *([dummy] * 7), dummy, 1 << 30, None) == L.STATUS[status]
+    assert lib.fa_bwd_dkdv(ctypes.byref(p), *([dummy] * 7), dummy, 1 << 30, None) == L.STATUS[status]
     assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 0
 
 
@@ -120,6 +132,24 @@ def test_null_and_alignment_rejected(lib, L):
     assert lib.fa_bwd(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, 16, None, 16, 1 << 20, None) == \
         L.STATUS["FA_ERR_NULL"]
     assert lib.fa_bwd(ctypes.byref(p), *([16] * 8), 8, 16, 1 << 20, None) == L.STATUS["FA_ERR_ALIGN"]
+
+
+def test_backward_stage_pointer_checks(lib, L):
+    p = _params(L)
+    ok = [16] * 7
+    NULL = L.STATUS["FA_ERR_NULL"]
+    for i in range(7):  # Q, K, V, O, LSE, dO, dQ all required by the dQ stage
+        args = list(ok)
+        args[i] = None
+        assert lib.fa_bwd_dq(ctypes.byref(p), *args, 16, 1 << 20, None) == NULL, i
+    for i in range(7):  # Q, K, V, LSE, dO, dK, dV all required by the dK/dV stage
+        args = list(ok)
+        args[i] = None
+        assert lib.fa_bwd_dkdv(ctypes.byref(p), *args, 16, 1 << 20, None) == NULL, i
+    assert lib.fa_bwd_dq(ctypes.byref(p), *ok, None, 1 << 20, None) == L.STATUS["FA_ERR_WORKSPACE"]
+    assert lib.fa_bwd_dkdv(ctypes.byref(p), *ok, 16, 4, None) == L.STATUS["FA_ERR_WORKSPACE"]
+    assert lib.fa_bwd_dkdv(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 40, 16, 1 << 20, None) == \
+        L.STATUS["FA_ERR_ALIGN"]
 
 
 def test_workspace_size_and_check(lib, L):
