@@ -35,8 +35,8 @@ struct TileShape {
 // ---------------------------------------------------------------------------
 // dQ (and D_i)
 // ---------------------------------------------------------------------------
-template <typename T, typename G, int D, int BC, bool DROP>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(AttnArgs a) {
+template <typename T, typename G, int D, int BC, bool DROP, int WPE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) bwd_dq_kernel(AttnArgs a) {
   using S = TileShape<T, D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
@@ -70,33 +70,29 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnArgs a) {
   const int q = q0w + lo;
   const bool qvalid = q < N;
 
+  // Rows past the end are clamped to row N-1 (never stored; their P is 0),
+  // so every load is unconditional.
+  const int qc = min(q, N - 1);
   frag qf[NC], dof[NC];
   float dpart = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int off = q * D + c * KI + hi * KH;
-    if (qvalid) {
-      qf[c] = load_frag<T>(Qg + off);
-      dof[c] = load_frag<T>(dOg + off);
-      const frag of = load_frag<T>(Og + off);
-      if constexpr (KH == 8) {
+    const int off = qc * D + c * KI + hi * KH;
+    qf[c] = load_frag<T>(Qg + off);
+    dof[c] = load_frag<T>(dOg + off);
+    const frag of = load_frag<T>(Og + off);
+    if constexpr (KH == 8) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) dpart += to_f32<T>(dof[c][t]) * to_f32<T>(of[t]);
-      } else {
-        dpart += dof[c] * of;
-      }
+      for (int t = 0; t < 8; ++t) dpart += to_f32<T>(dof[c][t]) * to_f32<T>(of[t]);
     } else {
-      qf[c] = zero_frag<T>();
-      dof[c] = zero_frag<T>();
+      dpart += dof[c] * of;
     }
   }
   const float Dq = dpart + swap_halves(dpart);
-  float lse2 = POS_INF;  // rows without a valid key (LSE = -inf) and padding rows get P = 0
-  if (qvalid) {
-    const float l = a.lse[(size_t)bh * N + q];
-    lse2 = (l == NEG_INF) ? POS_INF : l * kLog2e;
-    if (hi == 0) a.delta[(size_t)bh * N + q] = Dq;
-  }
+  // Rows without a valid key (LSE = -inf) and padding rows get P = 0.
+  const float lraw = a.lse[(size_t)bh * N + qc];
+  const float lse2 = (!qvalid || lraw == NEG_INF) ? POS_INF : lraw * kLog2e;
+  if (qvalid && hi == 0) a.delta[(size_t)bh * N + q] = Dq;
   uint32_t rowhash = 0;
   if constexpr (DROP) {
     const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
@@ -106,7 +102,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnArgs a) {
   const int kend = a.causal ? min(N, qtile0 + BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
   const uint8_t* bmrow = a.bmask ? a.bmask + (size_t)(qtile0 / a.mask_block) * a.nb : nullptr;
-  auto kept = [&](int j) { return bmrow == nullptr || bmrow[(j * BC) / a.mask_block] != 0; };
+  auto kept = [&](int j) { return bmrow == nullptr || mask_kept(bmrow, (j * BC) / a.mask_block); };
   auto next_kept = [&](int j) {
     ++j;
     while (j < ntiles && !kept(j)) ++j;
@@ -120,10 +116,9 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnArgs a) {
     for (int i = 0; i < NLD; ++i) {
       const int c = i * 256 + tid;
       const int row = c / S::KCH, ch = c % S::KCH;
-      const int key = k0 + row;
-      const size_t off = (size_t)key * D + ch * S::EPC;
-      kreg[i] = key < N ? *reinterpret_cast<const u32x4*>(Kg + off) : u32x4{0, 0, 0, 0};
-      vreg[i] = key < N ? *reinterpret_cast<const u32x4*>(Vg + off) : u32x4{0, 0, 0, 0};
+      const size_t off = (size_t)min(k0 + row, N - 1) * D + ch * S::EPC;
+      kreg[i] = *reinterpret_cast<const u32x4*>(Kg + off);
+      vreg[i] = *reinterpret_cast<const u32x4*>(Vg + off);
     }
   };
   auto sstore = [&](int buf) {
@@ -150,7 +145,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnArgs a) {
 
   while (j < ntiles) {
     const int jn = next_kept(j);
-    if (jn < ntiles) gload(jn);
+    gload(jn < ntiles ? jn : j);  // unconditional prefetch (see the forward kernel)
     const T* Ks = &smem[cur][0];
     const T* Vs = &smem[cur][TILE];
     const int k0 = j * BC;
@@ -214,7 +209,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnArgs a) {
           }
       }
     }
-    if (jn < ntiles) sstore(cur ^ 1);
+    sstore(cur ^ 1);
     __syncthreads();
     cur ^= 1;
     j = jn;
@@ -234,8 +229,8 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // dK and dV
 // ---------------------------------------------------------------------------
-template <typename T, typename G, int D, int BR, bool DROP>
-__global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnArgs a) {
+template <typename T, typename G, int D, int BR, bool DROP, int WPE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) bwd_dkdv_kernel(AttnArgs a) {
   using S = TileShape<T, D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
@@ -273,12 +268,14 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnArgs a) {
   const int key = k0w + lo;
   const bool kvalid = key < N;
 
+  // Keys past the end are clamped to row N-1: their scores are masked and
+  // their gradients never stored.
   frag kf[NC], vf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int off = key * D + c * KI + hi * KH;
-    kf[c] = kvalid ? load_frag<T>(Kg + off) : zero_frag<T>();
-    vf[c] = kvalid ? load_frag<T>(Vg + off) : zero_frag<T>();
+    const int off = min(key, N - 1) * D + c * KI + hi * KH;
+    kf[c] = load_frag<T>(Kg + off);
+    vf[c] = load_frag<T>(Vg + off);
   }
   uint32_t hk = 0;
   if constexpr (DROP) hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
@@ -289,7 +286,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnArgs a) {
   const int istart = a.causal ? (k0wg / BR) : 0;
   const int cblk = k0wg / a.mask_block;
   auto kept = [&](int i) {
-    return a.bmask == nullptr || a.bmask[(size_t)((i * BR) / a.mask_block) * a.nb + cblk] != 0;
+    return a.bmask == nullptr || mask_kept(a.bmask, ((i * BR) / a.mask_block) * a.nb + cblk);
   };
   auto next_kept = [&](int i) {
     ++i;
@@ -306,22 +303,18 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnArgs a) {
     for (int i = 0; i < NLD; ++i) {
       const int c = i * 256 + tid;
       const int row = c / S::KCH, ch = c % S::KCH;
-      const int qi = i0 + row;
-      const size_t off = (size_t)qi * D + ch * S::EPC;
-      qreg[i] = qi < N ? *reinterpret_cast<const u32x4*>(Qg + off) : u32x4{0, 0, 0, 0};
-      oreg[i] = qi < N ? *reinterpret_cast<const u32x4*>(dOg + off) : u32x4{0, 0, 0, 0};
+      const size_t off = (size_t)min(i0 + row, N - 1) * D + ch * S::EPC;
+      qreg[i] = *reinterpret_cast<const u32x4*>(Qg + off);
+      oreg[i] = *reinterpret_cast<const u32x4*>(dOg + off);
     }
-    if (tid < BR) {
-      const int qi = i0 + tid;
-      l_reg = POS_INF;
-      d_reg = 0.f;
-      if (qi < N) {
-        const float l = Lg[qi];
-        l_reg = (l == NEG_INF) ? POS_INF : l * kLog2e;
-        d_reg = Dg[qi];
-      }
-      if constexpr (DROP) h_reg = fmix32(hk ^ (uint32_t)qi);
-    }
+    // Row statistics of the tile: every lane loads (clamped), lanes < BR keep.
+    // Padding rows (and rows with no valid key) get log2-LSE = +inf, so P = 0.
+    const int qi = i0 + (tid % BR);
+    const int qic = min(qi, N - 1);
+    const float l = Lg[qic];
+    l_reg = (qi >= N || l == NEG_INF) ? POS_INF : l * kLog2e;
+    d_reg = Dg[qic];
+    if constexpr (DROP) h_reg = fmix32(hk ^ (uint32_t)qi);
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -355,7 +348,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnArgs a) {
 
   while (it < nqt) {
     const int itn = next_kept(it);
-    if (itn < nqt) gload(itn);
+    gload(itn < nqt ? itn : it);  // unconditional prefetch (see the forward kernel)
     const T* Qs = &smem[cur][0];
     const T* dOs = &smem[cur][TILE];
     const int i0 = it * BR;
@@ -439,7 +432,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnArgs a) {
           }
       }
     }
-    if (itn < nqt) sstore(cur ^ 1);
+    sstore(cur ^ 1);
     __syncthreads();
     cur ^= 1;
     it = itn;
@@ -462,16 +455,26 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
+// Resident waves per SIMD: two wherever the kernel fits 256 VGPRs without
+// spilling (16-bit inputs: the d = 64 kernels and the d = 128 dQ kernel
+// without dropout); the d = 128 dK/dV kernel holds K, V, dK and dV for its
+// keys and runs one, as do the fp32 kernels.
+template <typename T, int D, bool DROP> struct BwdOccupancy {
+  static constexpr bool h = sizeof(T) == 2;
+  static constexpr int dq = (h && (D == 64 || !DROP)) ? 2 : 1;
+  static constexpr int dkdv = (h && D == 64) ? 2 : 1;
+};
+
 template <typename T, typename G, int D, int BC, int BR, bool DROP>
 static hipError_t launch_bwd_t(int stage, const AttnArgs& a, hipStream_t s) {
   const int nt = (a.N + 127) / 128;  // 128-row query tiles (dQ) and 128-row key tiles (dK/dV)
   if (stage & 1) {
-    bwd_dq_kernel<T, G, D, BC, DROP><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
+    bwd_dq_kernel<T, G, D, BC, DROP, BwdOccupancy<T, D, DROP>::dq><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stage & 2) {
-    bwd_dkdv_kernel<T, G, D, BR, DROP><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
+    bwd_dkdv_kernel<T, G, D, BR, DROP, BwdOccupancy<T, D, DROP>::dkdv><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -162,6 +162,21 @@ __device__ __forceinline__ typename Mfma<T>::frag load_frag_tr(const T* tile, in
   return __builtin_bit_cast(typename Mfma<T>::frag, xy);
 }
 
+// Whether byte `idx` of a block mask is nonzero. `idx` must be uniform across
+// the wave: the aligned dword holding the byte is read with a scalar load
+// (constant address space), which keeps the vector-memory counter free for
+// the tile prefetches. The dword never leaves the 4-byte-aligned word that
+// holds the byte, so it stays inside the mask's page.
+__device__ __forceinline__ bool mask_kept(const uint8_t* bm, int idx) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(bm) + (uintptr_t)idx;
+  const __attribute__((address_space(4))) uint32_t* w =
+      (const __attribute__((address_space(4))) uint32_t*)(a & ~(uintptr_t)3);
+  return ((*w >> (8u * (uint32_t)(a & 3))) & 0xFFu) != 0;
+}
+
+// True if `pred` holds in any lane of the wave.
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
 // Stores 4 consecutive fp32 values as type G (one vector store).
 template <typename G>
 __device__ __forceinline__ void store4(G* p, float x0, float x1, float x2, float x3) {

@@ -21,8 +21,8 @@
 //   until the epilogue;
 //   dropout keep bits from the counter hash (fused step after softmax);
 //   O^T += V^T P^T on MFMA: the softmaxed S^T accumulators, rounded to the
-//   input type, are directly the B operand, so P never touches LDS; V is
-//   stored transposed in LDS so that A-operand reads are contiguous.
+//   input type, are directly the B operand, so P never touches LDS; the V^T
+//   A operand is read from the row-major V tile with LDS transpose reads.
 // Epilogue: O = O / l / (1 - p), LSE = m + log l (natural log).
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -33,17 +33,21 @@ template <typename T, int D, int BC>
 struct FwdCfg {
   static constexpr int BR = 128;                            // queries per workgroup
   static constexpr int EPC = 16 / sizeof(T);                // elements per 16-byte chunk
-  static constexpr int KS = D + (sizeof(T) == 2 ? 8 : 4);   // K tile row stride (elements)
-  static constexpr int VS = BC + (sizeof(T) == 2 ? 4 : 1);  // V^T tile row stride (elements)
+  static constexpr int KS = D + (sizeof(T) == 2 ? 8 : 4);   // K/V tile row stride (elements)
   static constexpr int KCH = D / EPC;                       // 16-byte chunks per K/V row
-  static constexpr int NLD = BC * KCH / 256;                // 16-byte loads per lane per tile
-  static constexpr int BUF = BC * KS + D * VS;              // elements per LDS buffer
+  static constexpr int NLD = BC * KCH / 256;                // 16-byte loads per lane per tensor per tile
+  static constexpr int TILE = BC * KS;                      // elements per K (or V) tile
   static_assert(BC % 32 == 0 && (BC * KCH) % 256 == 0, "tile shape");
-  static_assert((BC * KS * sizeof(T)) % 16 == 0, "V^T base alignment");
+  static_assert((TILE * sizeof(T)) % 16 == 0, "V tile base alignment");
 };
 
-template <typename T, int D, int BC, bool DROP>
-__global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
+// Rows whose running maximum grew by at most this much (log2 units) keep the
+// stale maximum: exponents stay below 2^8, which fp32 sums and the 8-bit
+// exponent of bf16/fp16-rounded P absorb, and the O rescale is skipped.
+constexpr float kLazyRescale = 8.0f;
+
+template <typename T, int D, int BC, bool DROP, int WPE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) fwd_kernel(AttnArgs a) {
   using C = FwdCfg<T, D, BC>;
   using M = Mfma<T>;
   using frag = typename M::frag;
@@ -53,7 +57,7 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
   constexpr int NC = D / KI;    // MFMA steps over d for S
   constexpr float NEG_INF = -__builtin_inff();
 
-  __shared__ __attribute__((aligned(16))) T smem[2 * C::BUF];
+  __shared__ __attribute__((aligned(16))) T smem[2][2 * C::TILE];  // [buffer][K tile | V tile], row-major
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lo = lane & 31, hi = lane >> 5;
@@ -62,11 +66,11 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
   // of the same query tile, so with B*H a multiple of 8 all tiles of a head
   // land on the same XCD (ids are dealt round-robin over the 8 XCDs) and
   // share its L2. Causal: longest rows first.
-  const int nq = (a.N + C::BR - 1) / C::BR;
+  const int N = a.N;
+  const int nq = (N + C::BR - 1) / C::BR;
   const int rank = blockIdx.x / a.BH;
   const int bh = blockIdx.x - rank * a.BH;
   const int qt = a.causal ? (nq - 1 - rank) : rank;
-  const int N = a.N;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const T* __restrict__ Qg = static_cast<const T*>(a.q) + hoff;
   const T* __restrict__ Kg = static_cast<const T*>(a.k) + hoff;
@@ -78,10 +82,14 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
   const int q = q0w + lo;
   const bool qvalid = q < N;
 
+  // Rows past the end are clamped to row N-1 (their results are masked or
+  // never stored), so every load is unconditional.
   frag qf[NC];
+  {
+    const int qc = min(q, N - 1);
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    qf[c] = qvalid ? load_frag<T>(Qg + q * D + c * KI + hi * KH) : zero_frag<T>();
+    for (int c = 0; c < NC; ++c) qf[c] = load_frag<T>(Qg + qc * D + c * KI + hi * KH);
+  }
 
   uint32_t rowhash = 0;
   if constexpr (DROP) {
@@ -94,7 +102,7 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
   const int kend = a.causal ? min(N, qtile0 + C::BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
   const uint8_t* bmrow = a.bmask ? a.bmask + (size_t)(qtile0 / a.mask_block) * a.nb : nullptr;
-  auto kept = [&](int j) { return bmrow == nullptr || bmrow[(j * BC) / a.mask_block] != 0; };
+  auto kept = [&](int j) { return bmrow == nullptr || mask_kept(bmrow, (j * BC) / a.mask_block); };
   auto next_kept = [&](int j) {
     ++j;
     while (j < ntiles && !kept(j)) ++j;
@@ -107,33 +115,19 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i) {
       const int c = i * 256 + tid;
-      const int row = c / C::KCH, ch = c % C::KCH;  // K: chunk index fastest
-      const int key = k0 + row;
-      kreg[i] = key < N ? *reinterpret_cast<const u32x4*>(Kg + key * D + ch * C::EPC) : u32x4{0, 0, 0, 0};
-      const int vrow = c % BC, vch = c / BC;       // V: key index fastest
-      const int vkey = k0 + vrow;
-      vreg[i] = vkey < N ? *reinterpret_cast<const u32x4*>(Vg + vkey * D + vch * C::EPC) : u32x4{0, 0, 0, 0};
+      const int row = c / C::KCH, ch = c % C::KCH;
+      const size_t off = (size_t)min(k0 + row, N - 1) * D + ch * C::EPC;
+      kreg[i] = *reinterpret_cast<const u32x4*>(Kg + off);
+      vreg[i] = *reinterpret_cast<const u32x4*>(Vg + off);
     }
   };
   auto sstore = [&](int buf) {
-    T* Ks = smem + buf * C::BUF;
-    T* Vt = Ks + BC * C::KS;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i) {
       const int c = i * 256 + tid;
       const int row = c / C::KCH, ch = c % C::KCH;
-      *reinterpret_cast<u32x4*>(Ks + row * C::KS + ch * C::EPC) = kreg[i];
-      const int vrow = c % BC, vch = c / BC;
-      if constexpr (sizeof(T) == 2) {
-        typedef T t8 __attribute__((ext_vector_type(8)));
-        const t8 e = __builtin_bit_cast(t8, vreg[i]);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) Vt[(vch * 8 + t) * C::VS + vrow] = e[t];
-      } else {
-        const f32x4 e = __builtin_bit_cast(f32x4, vreg[i]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) Vt[(vch * 4 + t) * C::VS + vrow] = e[t];
-      }
+      *reinterpret_cast<u32x4*>(&smem[buf][row * C::KS + ch * C::EPC]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&smem[buf][C::TILE + row * C::KS + ch * C::EPC]) = vreg[i];
     }
   };
 
@@ -152,10 +146,13 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
 
   while (j < ntiles) {
     const int jn = next_kept(j);
-    if (jn < ntiles) gload(jn);
+    // Always prefetch (the last iteration reloads its own tile into the idle
+    // buffer), so the loads are unconditional and the compiler's wait
+    // counting keeps them in flight across the compute below.
+    gload(jn < ntiles ? jn : j);
 
-    const T* Ks = smem + cur * C::BUF;
-    const T* Vt = Ks + BC * C::KS;
+    const T* Ks = &smem[cur][0];
+    const T* Vs = &smem[cur][C::TILE];
     const int k0 = j * BC;
     // The wave has work unless every key of the tile is above its diagonal.
     const bool active = (q0w < N) && (!a.causal || k0 <= q0w + 31);
@@ -188,9 +185,16 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
       mx = fmaxf(mx, swap_halves(mx));
       const float mnew = fmaxf(m_run, mx * a.sl2);
-      const float base = (mnew == NEG_INF) ? 0.f : mnew;
-      const float alpha = exp2_fast(m_run - base);
-      m_run = mnew;
+      if (wave_any(mnew > m_run + kLazyRescale)) {
+        const float alpha = exp2_fast(m_run - (mnew == NEG_INF ? 0.f : mnew));
+        m_run = mnew;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      }
+      const float base = (m_run == NEG_INF) ? 0.f : m_run;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -200,11 +204,7 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
           rs += p;
           s[kb][v] = p;
         }
-      l_run = l_run * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      l_run += rs;
 
       if constexpr (DROP) {
 #pragma unroll
@@ -216,6 +216,8 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
           }
       }
 
+      // O^T += V^T P^T: P^T is the B operand straight from registers; V^T
+      // comes from the row-major V tile through LDS transpose reads.
       if constexpr (KH == 8) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -223,12 +225,9 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
           for (int hf = 0; hf < 2; ++hf) {
             const frag pb = pack8<T>(s[kb][8 * hf + 0], s[kb][8 * hf + 1], s[kb][8 * hf + 2], s[kb][8 * hf + 3],
                                      s[kb][8 * hf + 4], s[kb][8 * hf + 5], s[kb][8 * hf + 6], s[kb][8 * hf + 7]);
-            const int kk = kb * 32 + 16 * hf + 4 * hi;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              const T* vp = Vt + (db * 32 + lo) * C::VS + kk;
-              o[db] = M::run(load_frag_2x4<T>(vp, vp + 8), pb, o[db]);
-            }
+            for (int db = 0; db < NDB; ++db)
+              o[db] = M::run(load_frag_tr<T>(Vs, C::KS, kb * 32 + 16 * hf, db * 32, lane), pb, o[db]);
           }
       } else {
 #pragma unroll
@@ -237,12 +236,12 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
           for (int v = 0; v < 16; ++v) {
             const int kk = kb * 32 + crow(v, hi);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = M::run(Vt[(db * 32 + lo) * C::VS + kk], s[kb][v], o[db]);
+            for (int db = 0; db < NDB; ++db) o[db] = M::run(Vs[kk * C::KS + db * 32 + lo], s[kb][v], o[db]);
           }
       }
     }
 
-    if (jn < ntiles) sstore(cur ^ 1);
+    sstore(cur ^ 1);
     __syncthreads();
     cur ^= 1;
     j = jn;
@@ -254,30 +253,21 @@ __global__ void __launch_bounds__(256) fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        T* op = Og + q * D + db * 32 + 8 * g + 4 * hi;
-        if constexpr (sizeof(T) == 2) {
-          typedef T t4 __attribute__((ext_vector_type(4)));
-          t4 r;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = static_cast<T>(o[db][4 * g + e] * inv);
-          *reinterpret_cast<t4*>(op) = r;
-        } else {
-          f32x4 r;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = o[db][4 * g + e] * inv;
-          *reinterpret_cast<f32x4*>(op) = r;
-        }
-      }
+      for (int g = 0; g < 4; ++g)
+        store4<T>(Og + q * D + db * 32 + 8 * g + 4 * hi, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
+                  o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
     if (hi == 0) a.lse[(size_t)bh * N + q] = lt > 0.f ? (m_run + log2_fast(lt)) * kLn2 : NEG_INF;
   }
 }
 
+// Two resident waves per SIMD (8 per CU) let one wave's softmax and LDS
+// work overlap the other's MFMAs; every instance fits 256 VGPRs without
+// spilling, and two workgroups' LDS buffers fit in the 160 KB of a CU.
 template <typename T, int D, int BC, bool DROP>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
   const int nq = (a.N + 127) / 128;
   const dim3 grid((unsigned)(nq * a.BH));
-  fwd_kernel<T, D, BC, DROP><<<grid, dim3(256), 0, s>>>(a);
+  fwd_kernel<T, D, BC, DROP, 2><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
