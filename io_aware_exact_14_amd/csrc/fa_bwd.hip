@@ -167,13 +167,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         }
       const bool need_mask = (a.causal && k0 + BC - 1 > q0w) || (k0 + BC > N);
       if (need_mask) {
+        // Same single-compare masking as the forward kernel.
+        const int t = (a.causal ? min(q, N - 1) : N - 1) - k0 - 4 * hi;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = k0 + kb * 32 + crow(v, hi);
-            if (key >= N || (a.causal && key > q)) s[kb][v] = NEG_INF;
-          }
+          for (int v = 0; v < 16; ++v)
+            if (kb * 32 + 8 * (v >> 2) + (v & 3) > t) s[kb][v] = NEG_INF;
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -229,7 +229,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 // ---------------------------------------------------------------------------
 // dK and dV
 // ---------------------------------------------------------------------------
-template <typename T, typename G, int D, int BR, bool DROP, int WPE>
+// VLDS: keep the workgroup's V rows in LDS (read as B fragments every tile)
+// instead of in registers, which frees 32 VGPRs per lane at d = 128.
+template <typename T, typename G, int D, int BR, bool DROP, int WPE, bool VLDS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) bwd_dkdv_kernel(AttnArgs a) {
   using S = TileShape<T, D>;
   using M = Mfma<T>;
@@ -246,6 +248,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   __shared__ __attribute__((aligned(16))) float side_l[2][BR];  // LSE in log2 units (+inf: no valid key)
   __shared__ __attribute__((aligned(16))) float side_d[2][BR];  // D_i
   __shared__ __attribute__((aligned(16))) uint32_t side_h[2][BR];  // dropout row hash
+  __shared__ __attribute__((aligned(16))) T vsm[VLDS ? BK * S::KS : 8];  // V rows of this workgroup
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lo = lane & 31, hi = lane >> 5;
@@ -270,12 +273,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 
   // Keys past the end are clamped to row N-1: their scores are masked and
   // their gradients never stored.
-  frag kf[NC], vf[NC];
+  frag kf[NC], vf[VLDS ? 1 : NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int off = min(key, N - 1) * D + c * KI + hi * KH;
     kf[c] = load_frag<T>(Kg + off);
-    vf[c] = load_frag<T>(Vg + off);
+    if constexpr (!VLDS) vf[c] = load_frag<T>(Vg + off);
+  }
+  if constexpr (VLDS) {
+    constexpr int NLV = BK * S::KCH / 256;
+#pragma unroll
+    for (int i = 0; i < NLV; ++i) {
+      const int c = i * 256 + tid;
+      const int row = c / S::KCH, ch = c % S::KCH;
+      *reinterpret_cast<u32x4*>(&vsm[row * S::KS + ch * S::EPC]) =
+          *reinterpret_cast<const u32x4*>(Vg + (size_t)min(k0wg + row, N - 1) * D + ch * S::EPC);
+    }
   }
   uint32_t hk = 0;
   if constexpr (DROP) hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
@@ -367,17 +380,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int qb = 0; qb < NQB; ++qb) {
           const int off = (qb * 32 + lo) * S::KS + c * KI + hi * KH;
           s[qb] = M::run(load_frag<T>(Qs + off), kf[c], s[qb]);
-          dp[qb] = M::run(load_frag<T>(dOs + off), vf[c], dp[qb]);
+          if constexpr (VLDS)
+            dp[qb] = M::run(load_frag<T>(dOs + off), load_frag<T>(&vsm[(w * 32 + lo) * S::KS + c * KI + hi * KH]),
+                            dp[qb]);
+          else
+            dp[qb] = M::run(load_frag<T>(dOs + off), vf[c], dp[qb]);
         }
       const bool need_mask = (a.causal && i0 < k0w + 31) || (k0w + 31 >= N);
       if (need_mask) {
+        // Hide queries below this lane's key (causal), or every query when
+        // the key is past the end: query - i0 is a compile-time offset plus
+        // 4*hi, so each element costs one compare.
+        const int t = (kvalid ? (a.causal ? key - i0 : -(1 << 30)) : (1 << 30)) - 4 * hi;
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int qi = i0 + qb * 32 + crow(v, hi);
-            if (!kvalid || (a.causal && key > qi)) s[qb][v] = NEG_INF;
-          }
+          for (int v = 0; v < 16; ++v)
+            if (qb * 32 + 8 * (v >> 2) + (v & 3) < t) s[qb][v] = NEG_INF;
       }
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
@@ -462,7 +481,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 template <typename T, int D, bool DROP> struct BwdOccupancy {
   static constexpr bool h = sizeof(T) == 2;
   static constexpr int dq = (h && (D == 64 || !DROP)) ? 2 : 1;
-  static constexpr int dkdv = (h && D == 64) ? 2 : 1;
+  static constexpr bool vlds = h && D == 128;
+  static constexpr int dkdv = h ? 2 : 1;
 };
 
 template <typename T, typename G, int D, int BC, int BR, bool DROP>
@@ -474,7 +494,8 @@ static hipError_t launch_bwd_t(int stage, const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (stage & 2) {
-    bwd_dkdv_kernel<T, G, D, BR, DROP, BwdOccupancy<T, D, DROP>::dkdv><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
+    using O = BwdOccupancy<T, D, DROP>;
+    bwd_dkdv_kernel<T, G, D, BR, DROP, O::dkdv, O::vlds><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -490,9 +511,9 @@ template <typename T>
 static hipError_t launch_bwd_16(bool f32grad, int d, bool dropout, int stage, const AttnArgs& a, hipStream_t s) {
   if (f32grad)
     return d == 64 ? launch_bwd_d<T, float, 64, 64, 64>(dropout, stage, a, s)
-                   : launch_bwd_d<T, float, 128, 64, 64>(dropout, stage, a, s);
+                   : launch_bwd_d<T, float, 128, 64, 32>(dropout, stage, a, s);
   return d == 64 ? launch_bwd_d<T, T, 64, 64, 64>(dropout, stage, a, s)
-                 : launch_bwd_d<T, T, 128, 64, 64>(dropout, stage, a, s);
+                 : launch_bwd_d<T, T, 128, 64, 32>(dropout, stage, a, s);
 }
 
 hipError_t launch_bwd(Elt t, Elt gt, int d, bool dropout, int stage, const AttnArgs& a, hipStream_t s) {

@@ -169,13 +169,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 
       const bool need_mask = (a.causal && k0 + BC - 1 > q0w) || (k0 + BC > N);
       if (need_mask) {
+        // Hide keys past min(q, N-1) (causal) or past N-1; key - k0 is a
+        // compile-time offset plus 4*hi, so each element costs one compare.
+        const int t = (a.causal ? min(q, N - 1) : N - 1) - k0 - 4 * hi;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = k0 + kb * 32 + crow(v, hi);
-            if (key >= N || (a.causal && key > q)) s[kb][v] = NEG_INF;
-          }
+          for (int v = 0; v < 16; ++v)
+            if (kb * 32 + 8 * (v >> 2) + (v & 3) > t) s[kb][v] = NEG_INF;
       }
 
       float mx = NEG_INF;
