@@ -474,57 +474,71 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
-// Resident waves per SIMD: two wherever the kernel fits 256 VGPRs without
-// spilling (16-bit inputs: the d = 64 kernels and the d = 128 dQ kernel
-// without dropout); the d = 128 dK/dV kernel holds K, V, dK and dV for its
-// keys and runs one, as do the fp32 kernels.
-template <typename T, int D, bool DROP> struct BwdOccupancy {
-  static constexpr bool h = sizeof(T) == 2;
-  static constexpr int dq = (h && (D == 64 || !DROP)) ? 2 : 1;
-  static constexpr bool vlds = h && D == 128;
-  static constexpr int dkdv = h ? 2 : 1;
-};
+// Launch configurations. A dQ workgroup streams BC-key tiles; a dK/dV
+// workgroup streams BR-query tiles; WPE is the resident waves per SIMD the
+// kernel is compiled for (more waves overlap one wave's softmax and LDS
+// work with another's MFMAs, at the price of registers). Short sequences
+// (causal rows of at most a few thousand keys) run few tiles per workgroup,
+// so they take small tiles and high occupancy; long ones take larger tiles,
+// which amortize the per-tile barrier and loads. With VLDS the dK/dV kernel
+// keeps the workgroup's V rows in LDS instead of registers.
+template <typename T, typename G, int D, bool DROP, int BC, int WPE>
+static hipError_t launch_dq(const AttnArgs& a, hipStream_t s) {
+  const int nt = (a.N + 127) / 128;
+  bwd_dq_kernel<T, G, D, BC, DROP, WPE><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
 
-template <typename T, typename G, int D, int BC, int BR, bool DROP>
-static hipError_t launch_bwd_t(int stage, const AttnArgs& a, hipStream_t s) {
-  const int nt = (a.N + 127) / 128;  // 128-row query tiles (dQ) and 128-row key tiles (dK/dV)
+template <typename T, typename G, int D, bool DROP, int BR, int WPE, bool VLDS>
+static hipError_t launch_dkdv(const AttnArgs& a, hipStream_t s) {
+  const int nt = (a.N + 127) / 128;
+  bwd_dkdv_kernel<T, G, D, BR, DROP, WPE, VLDS><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, typename G, int D, bool DROP>
+static hipError_t launch_bwd_cfg(int stage, const AttnArgs& a, hipStream_t s) {
+  constexpr bool h = sizeof(T) == 2;
+  hipError_t e = hipSuccess;
   if (stage & 1) {
-    bwd_dq_kernel<T, G, D, BC, DROP, BwdOccupancy<T, D, DROP>::dq><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
-    const hipError_t e = hipGetLastError();
+    if constexpr (!h)
+      e = launch_dq<T, G, D, DROP, D == 64 ? 64 : 32, 1>(a, s);
+    else if constexpr (D == 128)
+      e = launch_dq<T, G, D, DROP, 64, DROP ? 1 : 2>(a, s);
+    else
+      e = a.N <= 4096 ? launch_dq<T, G, D, DROP, 32, DROP ? 2 : 3>(a, s) : launch_dq<T, G, D, DROP, 64, 2>(a, s);
     if (e != hipSuccess) return e;
   }
   if (stage & 2) {
-    using O = BwdOccupancy<T, D, DROP>;
-    bwd_dkdv_kernel<T, G, D, BR, DROP, O::dkdv, O::vlds><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
-    return hipGetLastError();
+    if constexpr (!h)
+      e = launch_dkdv<T, G, D, DROP, D == 64 ? 64 : 32, 1, false>(a, s);
+    else if constexpr (D == 128)
+      e = launch_dkdv<T, G, D, DROP, 32, 2, true>(a, s);
+    else
+      e = a.N <= 2048 ? launch_dkdv<T, G, D, DROP, 32, DROP ? 2 : 3, true>(a, s)
+                      : launch_dkdv<T, G, D, DROP, 64, 2, false>(a, s);
   }
-  return hipSuccess;
+  return e;
 }
 
-template <typename T, typename G, int D, int BC, int BR>
-static hipError_t launch_bwd_d(bool dropout, int stage, const AttnArgs& a, hipStream_t s) {
-  return dropout ? launch_bwd_t<T, G, D, BC, BR, true>(stage, a, s)
-                 : launch_bwd_t<T, G, D, BC, BR, false>(stage, a, s);
-}
-
-template <typename T>
-static hipError_t launch_bwd_16(bool f32grad, int d, bool dropout, int stage, const AttnArgs& a, hipStream_t s) {
-  if (f32grad)
-    return d == 64 ? launch_bwd_d<T, float, 64, 64, 64>(dropout, stage, a, s)
-                   : launch_bwd_d<T, float, 128, 64, 32>(dropout, stage, a, s);
-  return d == 64 ? launch_bwd_d<T, T, 64, 64, 64>(dropout, stage, a, s)
-                 : launch_bwd_d<T, T, 128, 64, 32>(dropout, stage, a, s);
+template <typename T, typename G>
+static hipError_t launch_bwd_g(int d, bool dropout, int stage, const AttnArgs& a, hipStream_t s) {
+  if (d == 64)
+    return dropout ? launch_bwd_cfg<T, G, 64, true>(stage, a, s) : launch_bwd_cfg<T, G, 64, false>(stage, a, s);
+  return dropout ? launch_bwd_cfg<T, G, 128, true>(stage, a, s) : launch_bwd_cfg<T, G, 128, false>(stage, a, s);
 }
 
 hipError_t launch_bwd(Elt t, Elt gt, int d, bool dropout, int stage, const AttnArgs& a, hipStream_t s) {
+  const bool f32grad = gt == Elt::F32;
   switch (t) {
     case Elt::BF16:
-      return launch_bwd_16<__bf16>(gt == Elt::F32, d, dropout, stage, a, s);
+      return f32grad ? launch_bwd_g<__bf16, float>(d, dropout, stage, a, s)
+                     : launch_bwd_g<__bf16, __bf16>(d, dropout, stage, a, s);
     case Elt::F16:
-      return launch_bwd_16<_Float16>(gt == Elt::F32, d, dropout, stage, a, s);
+      return f32grad ? launch_bwd_g<_Float16, float>(d, dropout, stage, a, s)
+                     : launch_bwd_g<_Float16, _Float16>(d, dropout, stage, a, s);
     case Elt::F32:
-      return d == 64 ? launch_bwd_d<float, float, 64, 64, 64>(dropout, stage, a, s)
-                     : launch_bwd_d<float, float, 128, 32, 32>(dropout, stage, a, s);
+      return launch_bwd_g<float, float>(d, dropout, stage, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -174,6 +174,28 @@ __device__ __forceinline__ bool mask_kept(const uint8_t* bm, int idx) {
   return ((*w >> (8u * (uint32_t)(a & 3))) & 0xFFu) != 0;
 }
 
+// Buffer resource over `bytes` bytes starting at `base` (raw, unstrided).
+// Buffer loads whose per-lane offset falls outside return zeros and such
+// stores are dropped, so tails need no clamping or branches; the
+// per-lane (VGPR) offset carries the row offset because the scalar offset is
+// not part of the range check. `bytes` must fit in 31 bits (checked by the
+// host layer for every per-head tensor).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes < 0 ? 0 : bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, int voff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, voff, 0, 0);
+}
+__device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, int voff, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r, voff, 0, 0);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int voff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, 0, 0);
+}
+
 // True if `pred` holds in any lane of the wave.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

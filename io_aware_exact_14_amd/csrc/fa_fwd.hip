@@ -27,11 +27,13 @@
 #include "fa_device.h"
 #include "fa_kernels.h"
 
+
+
 namespace fa {
 
-template <typename T, int D, int BC>
+template <typename T, int D, int BC, int QB>
 struct FwdCfg {
-  static constexpr int BR = 128;                            // queries per workgroup
+  static constexpr int BR = 128 * QB;                       // queries per workgroup (4 waves x 32 x QB)
   static constexpr int EPC = 16 / sizeof(T);                // elements per 16-byte chunk
   static constexpr int KS = D + (sizeof(T) == 2 ? 8 : 4);   // K/V tile row stride (elements)
   static constexpr int KCH = D / EPC;                       // 16-byte chunks per K/V row
@@ -46,15 +48,21 @@ struct FwdCfg {
 // exponent of bf16/fp16-rounded P absorb, and the O rescale is skipped.
 constexpr float kLazyRescale = 8.0f;
 
-template <typename T, int D, int BC, bool DROP, int WPE>
+// QB: 32-query blocks per wave. Every K fragment and every V^T transpose read
+// taken from LDS feeds QB MFMAs, which divides the LDS read traffic per
+// flop by QB (LDS bandwidth, not MFMA, bounds a wave with a single block).
+// Wave w owns the query blocks w, w + 4, ... of the workgroup tile, so causal
+// work is spread evenly over the waves.
+template <typename T, int D, int BC, int QB, bool DROP, int WPE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) fwd_kernel(AttnArgs a) {
-  using C = FwdCfg<T, D, BC>;
+  using C = FwdCfg<T, D, BC, QB>;
   using M = Mfma<T>;
   using frag = typename M::frag;
   constexpr int KI = M::KI, KH = M::KH;
   constexpr int NKB = BC / 32;  // 32-key blocks per tile
   constexpr int NDB = D / 32;   // 32-column blocks of O^T
   constexpr int NC = D / KI;    // MFMA steps over d for S
+  constexpr int RB = D * (int)sizeof(T);  // bytes per row
   constexpr float NEG_INF = -__builtin_inff();
 
   __shared__ __attribute__((aligned(16))) T smem[2][2 * C::TILE];  // [buffer][K tile | V tile], row-major
@@ -72,29 +80,38 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int bh = blockIdx.x - rank * a.BH;
   const int qt = a.causal ? (nq - 1 - rank) : rank;
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const T* __restrict__ Qg = static_cast<const T*>(a.q) + hoff;
   const T* __restrict__ Kg = static_cast<const T*>(a.k) + hoff;
   const T* __restrict__ Vg = static_cast<const T*>(a.v) + hoff;
-  T* __restrict__ Og = static_cast<T*>(a.out) + hoff;
 
   const int qtile0 = qt * C::BR;
-  const int q0w = qtile0 + w * 32;
-  const int q = q0w + lo;
-  const bool qvalid = q < N;
-
-  // Rows past the end are clamped to row N-1 (their results are masked or
-  // never stored), so every load is unconditional.
-  frag qf[NC];
-  {
-    const int qc = min(q, N - 1);
+  int q0b[QB], qb_[QB];  // first query of each of this wave's blocks; this lane's query
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = load_frag<T>(Qg + qc * D + c * KI + hi * KH);
+  for (int b = 0; b < QB; ++b) {
+    q0b[b] = qtile0 + (w + 4 * b) * 32;
+    qb_[b] = q0b[b] + lo;
   }
+  const int qlast = q0b[QB - 1] + 31;  // the wave's highest query
 
-  uint32_t rowhash = 0;
+  // Buffer accesses: rows past the end read as zeros (their scores are
+  // masked) and their stores are dropped.
+  const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(static_cast<const T*>(a.q) + hoff, N * RB);
+  frag qf[QB][NC];
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if constexpr (KH == 8)
+        qf[b][c] = __builtin_bit_cast(frag, buffer_load16(qrs, qb_[b] * RB + (c * KI + hi * KH) * (int)sizeof(T)));
+      else
+        qf[b][c] =
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qrs, qb_[b] * RB + (c * KI + hi) * 4, 0, 0));
+    }
+
+  uint32_t rowhash[QB];
   if constexpr (DROP) {
     const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
-    rowhash = fmix32(hk ^ (uint32_t)q);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) rowhash[b] = fmix32(hk ^ (uint32_t)qb_[b]);
   }
 
   // KV tiles this workgroup visits: causal stops at its diagonal; a block
@@ -109,16 +126,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     return j;
   };
 
+  // Lane-constant byte offsets of this lane's 16-byte chunks within a tile.
+  int voff[C::NLD];
+#pragma unroll
+  for (int i = 0; i < C::NLD; ++i) {
+    const int c = i * 256 + tid;
+    voff[i] = (c / C::KCH) * RB + (c % C::KCH) * 16;
+  }
   u32x4 kreg[C::NLD], vreg[C::NLD];
   auto gload = [&](int jt) {
     const int k0 = jt * BC;
+    const int rem = (N - k0) * RB;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (size_t)k0 * D, rem);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (size_t)k0 * D, rem);
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i) {
-      const int c = i * 256 + tid;
-      const int row = c / C::KCH, ch = c % C::KCH;
-      const size_t off = (size_t)min(k0 + row, N - 1) * D + ch * C::EPC;
-      kreg[i] = *reinterpret_cast<const u32x4*>(Kg + off);
-      vreg[i] = *reinterpret_cast<const u32x4*>(Vg + off);
+      kreg[i] = buffer_load16(kr, voff[i]);
+      vreg[i] = buffer_load16(vr, voff[i]);
     }
   };
   auto sstore = [&](int buf) {
@@ -131,10 +155,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     }
   };
 
-  f32x16 o[NDB];
+  f32x16 o[QB][NDB];
+  float m_run[QB], l_run[QB];  // l_run: per-lane partial row sums
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = zero16();
-  float m_run = NEG_INF, l_run = 0.f;
+  for (int b = 0; b < QB; ++b) {
+    m_run[b] = NEG_INF;
+    l_run[b] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[b][db] = zero16();
+  }
 
   int j = kept(0) ? 0 : next_kept(0);
   int cur = 0;
@@ -154,67 +183,75 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const T* Ks = &smem[cur][0];
     const T* Vs = &smem[cur][C::TILE];
     const int k0 = j * BC;
-    // The wave has work unless every key of the tile is above its diagonal.
-    const bool active = (q0w < N) && (!a.causal || k0 <= q0w + 31);
+    // The wave has work unless every key of the tile is above all its rows.
+    const bool active = (q0b[0] < N) && (!a.causal || k0 <= qlast);
     if (active) {
-      f32x16 s[NKB];
+      f32x16 s[QB][NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
+      for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[b][kb] = zero16();
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          s[kb] = M::run(load_frag<T>(Ks + (kb * 32 + lo) * C::KS + c * KI + hi * KH), qf[c], s[kb]);
-      }
-
-      const bool need_mask = (a.causal && k0 + BC - 1 > q0w) || (k0 + BC > N);
-      if (need_mask) {
-        // Hide keys past min(q, N-1) (causal) or past N-1; key - k0 is a
-        // compile-time offset plus 4*hi, so each element costs one compare.
-        const int t = (a.causal ? min(q, N - 1) : N - 1) - k0 - 4 * hi;
+        for (int kb = 0; kb < NKB; ++kb) {
+          const frag kf = load_frag<T>(Ks + (kb * 32 + lo) * C::KS + c * KI + hi * KH);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (kb * 32 + 8 * (v >> 2) + (v & 3) > t) s[kb][v] = NEG_INF;
-      }
-
-      float mx = NEG_INF;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float mnew = fmaxf(m_run, mx * a.sl2);
-      if (wave_any(mnew > m_run + kLazyRescale)) {
-        const float alpha = exp2_fast(m_run - (mnew == NEG_INF ? 0.f : mnew));
-        m_run = mnew;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-      }
-      const float base = (m_run == NEG_INF) ? 0.f : m_run;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = exp2_fast(fmaf(s[kb][v], a.sl2, -base));
-          rs += p;
-          s[kb][v] = p;
+          for (int b = 0; b < QB; ++b) s[b][kb] = M::run(kf, qf[b][c], s[b][kb]);
         }
-      l_run += rs;
+      }
 
-      if constexpr (DROP) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const bool need_mask = (a.causal && k0 + BC - 1 > q0b[b]) || (k0 + BC > N);
+        if (need_mask) {
+          // Hide keys past min(q, N-1) (causal) or past N-1; key - k0 is a
+          // compile-time offset plus 4*hi, so each element costs one compare.
+          const int t = (a.causal ? min(qb_[b], N - 1) : N - 1) - k0 - 4 * hi;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (kb * 32 + 8 * (v >> 2) + (v & 3) > t) s[b][kb][v] = NEG_INF;
+        }
+
+        float mx = NEG_INF;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][kb][v]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float mnew = fmaxf(m_run[b], mx * a.sl2);
+        if (wave_any(mnew > m_run[b] + kLazyRescale)) {
+          const float alpha = exp2_fast(m_run[b] - (mnew == NEG_INF ? 0.f : mnew));
+          m_run[b] = mnew;
+          l_run[b] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[b][db][v] *= alpha;
+        }
+        const float base = (m_run[b] == NEG_INF) ? 0.f : m_run[b];
+        float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const uint32_t key = (uint32_t)(k0 + kb * 32 + crow(v, hi));
-            if (fmix32(rowhash ^ key) < a.thresh) s[kb][v] = 0.f;
+            const float p = exp2_fast(fmaf(s[b][kb][v], a.sl2, -base));
+            rs += p;
+            s[b][kb][v] = p;
           }
+        l_run[b] += rs;
+
+        if constexpr (DROP) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const uint32_t key = (uint32_t)(k0 + kb * 32 + crow(v, hi));
+              if (fmix32(rowhash[b] ^ key) < a.thresh) s[b][kb][v] = 0.f;
+            }
+        }
       }
 
       // O^T += V^T P^T: P^T is the B operand straight from registers; V^T
@@ -224,11 +261,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const frag pb = pack8<T>(s[kb][8 * hf + 0], s[kb][8 * hf + 1], s[kb][8 * hf + 2], s[kb][8 * hf + 3],
-                                     s[kb][8 * hf + 4], s[kb][8 * hf + 5], s[kb][8 * hf + 6], s[kb][8 * hf + 7]);
+            frag pb[QB];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              o[db] = M::run(load_frag_tr<T>(Vs, C::KS, kb * 32 + 16 * hf, db * 32, lane), pb, o[db]);
+            for (int b = 0; b < QB; ++b)
+              pb[b] = pack8<T>(s[b][kb][8 * hf + 0], s[b][kb][8 * hf + 1], s[b][kb][8 * hf + 2], s[b][kb][8 * hf + 3],
+                               s[b][kb][8 * hf + 4], s[b][kb][8 * hf + 5], s[b][kb][8 * hf + 6], s[b][kb][8 * hf + 7]);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              const frag vt = load_frag_tr<T>(Vs, C::KS, kb * 32 + 16 * hf, db * 32, lane);
+#pragma unroll
+              for (int b = 0; b < QB; ++b) o[b][db] = M::run(vt, pb[b], o[b][db]);
+            }
           }
       } else {
 #pragma unroll
@@ -237,7 +280,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
           for (int v = 0; v < 16; ++v) {
             const int kk = kb * 32 + crow(v, hi);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = M::run(Vs[kk * C::KS + db * 32 + lo], s[kb][v], o[db]);
+            for (int db = 0; db < NDB; ++db) {
+              const float vt = Vs[kk * C::KS + db * 32 + lo];
+#pragma unroll
+              for (int b = 0; b < QB; ++b) o[b][db] = M::run(vt, s[b][kb][v], o[b][db]);
+            }
           }
       }
     }
@@ -248,43 +295,62 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     j = jn;
   }
 
-  const float lt = l_run + swap_halves(l_run);
-  const float inv = lt > 0.f ? a.rp / lt : 0.f;
-  if (qvalid) {
+  const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(static_cast<T*>(a.out) + hoff, N * RB);
+  const __amdgpu_buffer_rsrc_t lrs = buffer_rsrc(a.lse + (size_t)bh * N, N * 4);
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const float lt = l_run[b] + swap_halves(l_run[b]);
+    const float inv = lt > 0.f ? a.rp / lt : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store4<T>(Og + q * D + db * 32 + 8 * g + 4 * hi, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
-                  o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-    if (hi == 0) a.lse[(size_t)bh * N + q] = lt > 0.f ? (m_run + log2_fast(lt)) * kLn2 : NEG_INF;
+      for (int g = 0; g < 4; ++g) {
+        const int off = qb_[b] * RB + (db * 32 + 8 * g + 4 * hi) * (int)sizeof(T);
+        if constexpr (sizeof(T) == 2) {
+          typedef T t4 __attribute__((ext_vector_type(4)));
+          t4 r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = static_cast<T>(o[b][db][4 * g + e] * inv);
+          buffer_store8(ors, off, __builtin_bit_cast(u32x2, r));
+        } else {
+          f32x4 r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = o[b][db][4 * g + e] * inv;
+          buffer_store16(ors, off, __builtin_bit_cast(u32x4, r));
+        }
+      }
+    // One writer per row (lanes of the upper half aim past the end and are dropped).
+    buffer_store4(lrs, hi ? 0x7FFFFFF0 : qb_[b] * 4, lt > 0.f ? (m_run[b] + log2_fast(lt)) * kLn2 : NEG_INF);
   }
 }
 
-// Two resident waves per SIMD (8 per CU) let one wave's softmax and LDS
-// work overlap the other's MFMAs; every instance fits 256 VGPRs without
-// spilling, and two workgroups' LDS buffers fit in the 160 KB of a CU.
-template <typename T, int D, int BC, bool DROP>
+// Resident waves per SIMD: with one wave, softmax VALU work, LDS reads and
+// MFMAs of a tile run back to back; more waves let them overlap. d = 128
+// fits two waves (256 VGPRs, two workgroups' LDS in the 160 KB of a CU);
+// the 16-bit d = 64 kernel without dropout is held to 128 VGPRs for four
+// (a 16-byte spill, cheaper than the lost occupancy).
+template <typename T, int D, int BC, int QB, bool DROP>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
-  const int nq = (a.N + 127) / 128;
+  const int nq = (a.N + 128 * QB - 1) / (128 * QB);
   const dim3 grid((unsigned)(nq * a.BH));
-  fwd_kernel<T, D, BC, DROP, 2><<<grid, dim3(256), 0, s>>>(a);
+  constexpr int WPE = D * QB > 128 ? 1 : (D == 64 && !DROP && sizeof(T) == 2 ? 4 : 2);  // two query blocks at d = 128 need the whole register file
+  fwd_kernel<T, D, BC, QB, DROP, WPE><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 
-template <typename T, int D, int BC>
+template <typename T, int D, int BC, int QB>
 static hipError_t launch_fwd_d(bool dropout, const AttnArgs& a, hipStream_t s) {
-  return dropout ? launch_fwd_t<T, D, BC, true>(a, s) : launch_fwd_t<T, D, BC, false>(a, s);
+  return dropout ? launch_fwd_t<T, D, BC, QB, true>(a, s) : launch_fwd_t<T, D, BC, QB, false>(a, s);
 }
 
 hipError_t launch_fwd(Elt t, int d, bool dropout, const AttnArgs& a, hipStream_t s) {
   switch (t) {
     case Elt::BF16:
-      return d == 64 ? launch_fwd_d<__bf16, 64, 64>(dropout, a, s) : launch_fwd_d<__bf16, 128, 64>(dropout, a, s);
+      return d == 64 ? launch_fwd_d<__bf16, 64, 64, 1>(dropout, a, s) : launch_fwd_d<__bf16, 128, 64, 1>(dropout, a, s);
     case Elt::F16:
-      return d == 64 ? launch_fwd_d<_Float16, 64, 64>(dropout, a, s) : launch_fwd_d<_Float16, 128, 64>(dropout, a, s);
+      return d == 64 ? launch_fwd_d<_Float16, 64, 64, 1>(dropout, a, s) : launch_fwd_d<_Float16, 128, 64, 1>(dropout, a, s);
     case Elt::F32:
-      return d == 64 ? launch_fwd_d<float, 64, 64>(dropout, a, s) : launch_fwd_d<float, 128, 32>(dropout, a, s);
+      return d == 64 ? launch_fwd_d<float, 64, 64, 1>(dropout, a, s) : launch_fwd_d<float, 128, 32, 1>(dropout, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -143,3 +143,10 @@ def test_keep_bits_used_inside_backward(fa, p):
                 lvl = (g - g.min(axis=1, keepdims=True)) * (1 - p)
                 np.testing.assert_array_equal(np.rint(lvl).astype(bool), Z)
                 assert np.abs(lvl - np.rint(lvl)).max() < 0.05
+
+
+@pytest.mark.parametrize("N", [2100, 4500])
+@pytest.mark.parametrize("causal,p", [(True, 0.0), (False, 0.0), (True, 0.1)])
+def test_backward_long_rows(fa, N, causal, p):
+    # longer sequences take the large-tile launch configurations (with tails)
+    _check_bwd(fa, 1, 1, N, 64, torch.bfloat16, causal=causal, p=p, seed=0x5EED0003, in_seed=N + 5)
