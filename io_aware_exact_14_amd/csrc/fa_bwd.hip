@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
       dpart += dof[c] * of;
     }
   }
-  const float Dq = dpart + swap_halves(dpart);
+  const float Dq = half_sum(dpart);
   // Rows without a valid key (LSE = -inf) and padding rows get P = 0.
   const float lraw = a.lse[(size_t)bh * N + qc];
   const float lse2 = (!qvalid || lraw == NEG_INF) ? POS_INF : lraw * kLog2e;

@@ -114,8 +114,10 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-// Exchange with the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Combine a value with the one held by the lane 32 positions away (the other
+// half of the wave); the result is the same in both lanes of the pair.
+__device__ __forceinline__ float half_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
+__device__ __forceinline__ float half_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
 // MurmurHash3 32-bit finalizer (Appleby, public domain).
 __device__ __forceinline__ uint32_t fmix32(uint32_t x) {

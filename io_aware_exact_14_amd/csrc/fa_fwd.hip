@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][kb][v]);
-        mx = fmaxf(mx, swap_halves(mx));
+        mx = half_max(mx);
         const float mnew = fmaxf(m_run[b], mx * a.sl2);
         if (wave_any(mnew > m_run[b] + kLazyRescale)) {
           const float alpha = exp2_fast(m_run[b] - (mnew == NEG_INF ? 0.f : mnew));
@@ -299,7 +299,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const __amdgpu_buffer_rsrc_t lrs = buffer_rsrc(a.lse + (size_t)bh * N, N * 4);
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const float lt = l_run[b] + swap_halves(l_run[b]);
+    const float lt = half_sum(l_run[b]);
     const float inv = lt > 0.f ? a.rp / lt : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
