@@ -59,7 +59,7 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,       /* B, H or N negative, or B*H*N*d too large */
+  FA_ERR_SHAPE = 2,       /* B, H or N negative, N*d*4 bytes >= 2^31, or too many tiles */
   FA_ERR_DTYPE = 3,       /* unknown dtype, or grad_dtype not FA_F32 / in_dtype */
   FA_ERR_HEADDIM = 4,     /* d not in {64, 128} */
   FA_ERR_DROPOUT = 5,     /* dropout_p not in [0, 1) */

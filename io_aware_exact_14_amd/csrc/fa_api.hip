@@ -20,8 +20,9 @@ int check(const fa_params* p) {
   if (p->d != 64 && p->d != 128) return FA_ERR_HEADDIM;
   if (p->in_dtype < FA_F32 || p->in_dtype > FA_BF16) return FA_ERR_DTYPE;
   if (p->grad_dtype != FA_F32 && p->grad_dtype != p->in_dtype) return FA_ERR_DTYPE;
-  // Per-head element offsets are 32-bit; the grid is one dimension.
-  if (p->N > kMaxI32 / p->d) return FA_ERR_SHAPE;
+  // Per-head byte offsets (rows x d x element size) are 32-bit; the grid is one dimension.
+  const int64_t elt = p->in_dtype == FA_F32 ? 4 : 2;
+  if (p->N > kMaxI32 / (p->d * 4) || p->N > kMaxI32 / (p->d * elt)) return FA_ERR_SHAPE;
   if (p->B > 0 && p->H > kMaxI32 / p->B) return FA_ERR_SHAPE;
   const int64_t bh = p->B * p->H;
   const int64_t tiles = (p->N + 127) / 128;

@@ -90,6 +90,8 @@ CASES = [
     (dict(N=-1), "FA_ERR_SHAPE"),
     (dict(B=-2), "FA_ERR_SHAPE"),
     (dict(N=2**31 // 64 + 1), "FA_ERR_SHAPE"),
+    (dict(N=2**31 // 256 + 1), "FA_ERR_SHAPE"),        # N*d*4 bytes of a per-head fp32 tensor >= 2^31
+    (dict(N=2**31 // 512 + 1, d=128), "FA_ERR_SHAPE"),
     (dict(in_dtype=7), "FA_ERR_DTYPE"),
     (dict(in_dtype=1, grad_dtype=2), "FA_ERR_DTYPE"),
     (dict(scale=0.0), "FA_ERR_SCALE"),
@@ -119,6 +121,7 @@ def test_invalid_params_rejected(lib, L, kw, status):
 
 def test_valid_params_accepted(lib, L):
     for kw in (dict(), dict(d=128), dict(in_dtype=0), dict(in_dtype=1, grad_dtype=1), dict(causal=1),
+               dict(N=2**31 // 512 - 1, d=128),
                dict(dropout_p=0.1, seed=2**64 - 1), dict(block_mask=16, mask_block=256), dict(N=0), dict(B=0)):
         assert lib.fa_check_params(ctypes.byref(_params(L, **kw))) == 0, kw
 
