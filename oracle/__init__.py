@@ -17,6 +17,8 @@ Parity status of each function (see the pins in ``tests/test_oracle_*.py``):
   forms, invariants, torch SDPA in fp64).
 * ``backward_head`` / ``backward``: pinned (central finite differences,
   torch autograd in fp64, identities).
+* ``backward_rows`` (dQ of selected rows): pinned by central finite
+  differences with respect to those rows of Q.
 * ``dropout_keep``: pinned for the mixing function by the published
   MurmurHash3 test vectors; the chaining of (seed, b, h, i, j) is this
   library's own definition ("parity unpinned" beyond that definition and the
@@ -30,4 +32,5 @@ from .attention import (  # noqa: F401
     forward,
     backward,
     forward_rows,
+    backward_rows,
 )

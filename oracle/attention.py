@@ -161,3 +161,20 @@ def forward_rows(q, k, v, scale, b, h, rows, causal=False, dropout_p=0.0, seed=0
     each row computed from its own definition (for spot checks at large N)."""
     return forward_head(q[b, h], k[b, h], v[b, h], scale, causal, dropout_p, seed, b, h,
                         block_mask, mask_block, rows=rows)
+
+
+def backward_rows(q, k, v, do, scale, b, h, rows, causal=False, dropout_p=0.0, seed=0,
+                  block_mask=None, mask_block=128):
+    """dQ of selected query rows of head (b, h) of [B][H][N][d] inputs. Row i
+    of dQ needs only row i of P and dP and D_i, so each row follows from its
+    own definition: dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j."""
+    rows = np.asarray(rows, dtype=np.int64)
+    qh, kh, vh, doh = (_f64(t[b, h]) for t in (q, k, v, do))
+    N = kh.shape[0]
+    valid = valid_mask(N, causal, block_mask, mask_block, rows)
+    _, _, P = _probabilities(qh[rows], kh, scale, valid)
+    dP = doh[rows] @ vh.T
+    if dropout_p > 0.0:
+        dP = dP * dropout_keep(seed, b, h, rows, np.arange(N), dropout_p) / (1.0 - dropout_p)
+    D = (P * dP).sum(axis=1)
+    return scale * ((P * (dP - D[:, None])) @ kh)

@@ -127,3 +127,26 @@ def test_batched_backward_matches_heads():
     np.testing.assert_array_equal(dq[1, 0], g["dq"])
     np.testing.assert_array_equal(dk[1, 0], g["dk"])
     np.testing.assert_array_equal(dv[1, 0], g["dv"])
+
+
+@pytest.mark.parametrize("causal,p", [(False, 0.0), (True, 0.0), (True, 0.25)])
+def test_backward_rows_matches_finite_differences(causal, p):
+    # dQ of a few rows from their own definition, against central differences
+    # of L = sum(O * dO) with respect to those rows of Q
+    B, H, N, d = 1, 2, 13, 3
+    rng = np.random.default_rng(61)
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    rows = [0, 5, 12]
+    kw = dict(causal=causal, dropout_p=p, seed=17)
+    g = oracle.backward_rows(q, k, v, do, 0.6, 0, 1, rows, **kw)
+    eps = 1e-6
+    for a, i in enumerate(rows):
+        for c in range(d):
+            qp, qm = q.copy(), q.copy()
+            qp[0, 1, i, c] += eps
+            qm[0, 1, i, c] -= eps
+            lp = (oracle.forward_head(qp[0, 1], k[0, 1], v[0, 1], 0.6, b=0, h=1, **kw)[0] * do[0, 1]).sum()
+            lm = (oracle.forward_head(qm[0, 1], k[0, 1], v[0, 1], 0.6, b=0, h=1, **kw)[0] * do[0, 1]).sum()
+            assert abs((lp - lm) / (2 * eps) - g[a, c]) < 1e-6
+    full = oracle.backward_head(q[0, 1], k[0, 1], v[0, 1], do[0, 1], 0.6, b=0, h=1, **kw)["dq"]
+    np.testing.assert_allclose(g, full[rows], atol=1e-12)
