@@ -17,8 +17,9 @@ Parity status of each function (see the pins in ``tests/test_oracle_*.py``):
   forms, invariants, torch SDPA in fp64).
 * ``backward_head`` / ``backward``: pinned (central finite differences,
   torch autograd in fp64, identities).
-* ``backward_rows`` (dQ of selected rows): pinned by central finite
-  differences with respect to those rows of Q.
+* ``backward_rows`` (dQ of selected rows) and ``backward_cols`` (dK, dV of
+  selected keys): pinned by central finite differences with respect to those
+  rows of Q, K and V.
 * ``dropout_keep``: pinned for the mixing function by the published
   MurmurHash3 test vectors; the chaining of (seed, b, h, i, j) is this
   library's own definition ("parity unpinned" beyond that definition and the
@@ -33,4 +34,5 @@ from .attention import (  # noqa: F401
     backward,
     forward_rows,
     backward_rows,
+    backward_cols,
 )

@@ -47,17 +47,18 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def valid_mask(N: int, causal: bool, block_mask=None, mask_block: int = 128, rows=None, M: int | None = None):
-    """Bool ``[len(rows)][M]``: which (query i, key j) pairs take part.
+def valid_mask(N: int, causal: bool, block_mask=None, mask_block: int = 128, rows=None, M: int | None = None,
+               cols=None):
+    """Bool ``[len(rows)][len(cols)]``: which (query i, key j) pairs take part.
 
-    ``rows`` defaults to all N query rows; ``M`` (number of keys) defaults to N.
-    Causal masking is square and top-left aligned: key j is hidden from query
-    i when j > i.
+    ``rows`` defaults to all N query rows; ``cols`` to all ``M`` keys (``M``
+    defaults to N). Causal masking is square and top-left aligned: key j is
+    hidden from query i when j > i.
     """
     M = N if M is None else M
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
-    cols = np.arange(M)
-    valid = np.ones((rows.size, M), dtype=bool)
+    cols = np.arange(M) if cols is None else np.asarray(cols, dtype=np.int64)
+    valid = np.ones((rows.size, cols.size), dtype=bool)
     if causal:
         valid &= cols[None, :] <= rows[:, None]
     if block_mask is not None:
@@ -178,3 +179,40 @@ def backward_rows(q, k, v, do, scale, b, h, rows, causal=False, dropout_p=0.0, s
         dP = dP * dropout_keep(seed, b, h, rows, np.arange(N), dropout_p) / (1.0 - dropout_p)
     D = (P * dP).sum(axis=1)
     return scale * ((P * (dP - D[:, None])) @ kh)
+
+
+def backward_cols(q, k, v, do, scale, b, h, cols, causal=False, dropout_p=0.0, seed=0,
+                  block_mask=None, mask_block=128, row_chunk=256):
+    """dK and dV of selected keys of head (b, h) of [B][H][N][d] inputs.
+
+    Key j's gradients sum over the rows i that see it, and each term needs
+    that row's full statistics (its LSE and D_i), so every such row is
+    computed whole from the definition:
+
+        dV_j = sum_i Pd_ij dO_i,   dK_j = scale * sum_i P_ij (dP_ij - D_i) Q_i
+
+    The sum over i runs over the rows in increasing order, ``row_chunk`` rows
+    at a time (the chunks only bound memory). Returns (dK [c][d], dV [c][d]).
+    """
+    cols = np.asarray(cols, dtype=np.int64)
+    qh, kh, vh, doh = (_f64(t[b, h]) for t in (q, k, v, do))
+    N, d = kh.shape
+    seen = valid_mask(N, causal, block_mask, mask_block, cols=cols).any(axis=1)
+    rows_all = np.nonzero(seen)[0]
+    dk = np.zeros((cols.size, d))
+    dv = np.zeros((cols.size, d))
+    for c0 in range(0, rows_all.size, row_chunk):
+        rows = rows_all[c0:c0 + row_chunk]
+        valid = valid_mask(N, causal, block_mask, mask_block, rows)
+        _, _, P = _probabilities(qh[rows], kh, scale, valid)
+        dP = doh[rows] @ vh.T
+        if dropout_p > 0.0:
+            Zs = dropout_keep(seed, b, h, rows, np.arange(N), dropout_p) / (1.0 - dropout_p)
+        else:
+            Zs = 1.0
+        dP = dP * Zs
+        D = (P * dP).sum(axis=1)
+        Pc = P[:, cols]
+        dv += (Pc * (Zs[:, cols] if dropout_p > 0.0 else 1.0)).T @ doh[rows]
+        dk += scale * ((Pc * (dP[:, cols] - D[:, None])).T @ qh[rows])
+    return dk, dv

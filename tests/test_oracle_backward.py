@@ -150,3 +150,33 @@ def test_backward_rows_matches_finite_differences(causal, p):
             assert abs((lp - lm) / (2 * eps) - g[a, c]) < 1e-6
     full = oracle.backward_head(q[0, 1], k[0, 1], v[0, 1], do[0, 1], 0.6, b=0, h=1, **kw)["dq"]
     np.testing.assert_allclose(g, full[rows], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,block,p", [(False, False, 0.0), (True, False, 0.0), (True, True, 0.25),
+                                            (False, True, 0.1)])
+def test_backward_cols_matches_finite_differences(causal, block, p):
+    # dK, dV of a few keys, against central differences of L = sum(O * dO)
+    # with respect to those rows of K and V (row_chunk=4 spans several chunks)
+    B, H, N, d, mb = 2, 1, 13, 3, 4
+    rng = np.random.default_rng(71)
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    bm = _bm(4, 72) if block else None
+    cols = [0, 6, 12]
+    kw = dict(causal=causal, dropout_p=p, seed=23, block_mask=bm, mask_block=mb)
+    gk, gv = oracle.backward_cols(q, k, v, do, 0.7, 1, 0, cols, row_chunk=4, **kw)
+
+    def loss(kk, vv):
+        return (oracle.forward_head(q[1, 0], kk, vv, 0.7, b=1, h=0, **kw)[0] * do[1, 0]).sum()
+
+    eps = 1e-6
+    for a, j in enumerate(cols):
+        for c in range(d):
+            for g, which in ((gk, 0), (gv, 1)):
+                xp = [k[1, 0].copy(), v[1, 0].copy()]
+                xm = [k[1, 0].copy(), v[1, 0].copy()]
+                xp[which][j, c] += eps
+                xm[which][j, c] -= eps
+                assert abs((loss(*xp) - loss(*xm)) / (2 * eps) - g[a, c]) < 1e-6
+    full = oracle.backward_head(q[1, 0], k[1, 0], v[1, 0], do[1, 0], 0.7, b=1, h=0, **kw)
+    np.testing.assert_allclose(gk, full["dk"][cols], atol=1e-12)
+    np.testing.assert_allclose(gv, full["dv"][cols], atol=1e-12)
