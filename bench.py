@@ -2,6 +2,8 @@
 """Throughput of tiled exact attention (forward + backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2]
+    python bench.py --standard [--workload C2]     standard vs tiled attention
+    python bench.py --sweep [--sweep-n 1024,...]   sequence-length sweep
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 fa_fwd (O, LSE), then the two backward stages fa_bwd_dq (D, dQ) and
@@ -12,6 +14,11 @@ causal). Prints ONE JSON line on stdout; per-kernel detail goes to stderr.
 
 FLOP convention: forward 4*B*H*N^2*d (halved when causal, kept-block count
 when block-sparse), backward 2.5x forward.
+
+``--standard`` times the same workload through standard attention (every
+N x N intermediate written to device memory) beside the tiled kernels, and
+``--sweep`` times the tiled kernels and their device-memory footprint over
+sequence lengths; each prints one JSON line of its own.
 """
 from __future__ import annotations
 
@@ -144,6 +151,281 @@ def cpu_baseline(w, x, target_s=12.0):
     }
 
 
+def standard_attention(q, k, v, do, scale, causal_mask=None):
+    """Standard attention, forward and backward, as a chain of PyTorch/ROCm
+    library kernels that write every N x N intermediate to device memory.
+
+    This is the algorithm the tiled method is measured against (FlashAttention
+    milestone page, "The idea": the standard implementation stores S and P in
+    HBM). Forward: S = scale Q K^T (batched GEMM, input-dtype output), masked
+    fill of S, P = softmax(S) (fp32 arithmetic inside, input-dtype storage),
+    O = P V. Backward: dV^T = dO^T P, dP = dO V^T, dS = P (dP - rowsum(P dP))
+    (PyTorch's fused softmax backward), dQ = scale dS K, dK^T = scale Q^T dS.
+    Every product takes contiguous operands: the N x d transposes are
+    materialized, the N x N matrices are never transposed. ``causal_mask`` is
+    a bool [N][N] device tensor, True where a key is hidden. Returns
+    (O, dQ, dK, dV) in the input dtype.
+    """
+    import torch
+
+    B, H, N, d = q.shape
+    BH = B * H
+    q3, k3, v3, do3 = (t.reshape(BH, N, d) for t in (q, k, v, do))
+    dt, dev = q.dtype, q.device
+    s = torch.empty(BH, N, N, dtype=dt, device=dev).baddbmm_(q3, k3.transpose(1, 2).contiguous(),
+                                                             beta=0.0, alpha=scale)
+    if causal_mask is not None:
+        s.masked_fill_(causal_mask, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    del s
+    o = torch.bmm(p, v3)
+    dvT = torch.bmm(do3.transpose(1, 2).contiguous(), p)
+    dp = torch.bmm(do3, v3.transpose(1, 2).contiguous())
+    ds = torch._softmax_backward_data(dp, p, -1, dt)
+    del dp, p
+    dq = torch.empty(BH, N, d, dtype=dt, device=dev).baddbmm_(ds, k3, beta=0.0, alpha=scale)
+    dkT = torch.empty(BH, d, N, dtype=dt, device=dev).baddbmm_(q3.transpose(1, 2).contiguous(), ds,
+                                                               beta=0.0, alpha=scale)
+    shape = (B, H, N, d)
+    return (o.reshape(shape), dq.reshape(shape), dkT.transpose(1, 2).reshape(shape),
+            dvT.transpose(1, 2).reshape(shape))
+
+
+def _tiled_step_fn(lib, p, q, k, v, do, o, lse, dq, dk, dv, ws, stream):
+    """One fwd + bwd pass through the C ABI (fa_fwd, fa_bwd_dq, fa_bwd_dkdv)."""
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    pp = ctypes.byref(p)
+    fwd_args = (pp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), sp)
+    dq_args = (pp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+               dq.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+    dkdv_args = (pp, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(), dk.data_ptr(),
+                 dv.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+
+    def fwd():
+        if lib.fa_fwd(*fwd_args) != 0:
+            raise RuntimeError("fa_fwd failed")
+
+    def bwd():
+        if lib.fa_bwd_dq(*dq_args) != 0 or lib.fa_bwd_dkdv(*dkdv_args) != 0:
+            raise RuntimeError("fa_bwd failed")
+
+    return fwd, bwd
+
+
+def _time_fwd_bwd(fwd, bwd, steps, warmup, stream):
+    """(ms per fwd+bwd step by wall clock, forward ms, backward ms by HIP events)."""
+    import torch
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    f = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    b = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    return ms, f, b
+
+
+def _peak_extra_bytes(run):
+    """Device memory a call allocates at its peak beyond what is already resident."""
+    import torch
+
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    out = run()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    del out
+    return int(peak)
+
+
+def read_step_traffic(workload: str):
+    """HBM bytes per fwd+bwd step of the standard and the tiled path from the
+    committed rocprofv3 counter summary ({} when absent; the tiled figure only
+    while the kernel sources are unchanged)."""
+    path = os.path.join(ROOT, "profiles", f"standard_vs_tiled__{workload}__traffic.txt")
+    if not os.path.exists(path):
+        return {}
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    out = {}
+    try:
+        out["standard"] = float(kv["standard_bytes_per_step"])
+        if kv.get("src_sha256") == src_digest():
+            out["tiled"] = float(kv["tiled_bytes_per_step"])
+    except (KeyError, ValueError):
+        pass
+    return out
+
+
+def run_standard(args):
+    """Standard vs tiled attention on one workload (no dropout, no block mask):
+    fwd/bwd time, convention TFLOP/s, peak extra device memory, and HBM bytes
+    per step from the committed counter summary."""
+    import numpy as np
+    import torch
+
+    import io_aware_exact_14_amd as fa
+    from io_aware_exact_14_amd import _lib
+    from workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.dropout_p > 0 or w.block_sparse or not w.backward:
+        print(f"--standard covers dense workloads with a backward pass (no dropout, no block mask); "
+              f"{w.name} is not one", file=sys.stderr)
+        return 2
+    x = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    stream = torch.cuda.current_stream()
+    lib = _lib.load()
+    p = fa.params(w.B, w.H, w.N, w.d, w.torch_dtype, scale=w.scale, causal=w.causal)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(max(int(lib.fa_bwd_workspace_bytes(ctypes.byref(p))), 1), dtype=torch.uint8, device=dev)
+    t_fwd, t_bwd = _tiled_step_fn(lib, p, q, k, v, do, o, lse, dq, dk, dv, ws, stream)
+    mask = (torch.ones(w.N, w.N, dtype=torch.bool).triu_(1).to(dev)) if w.causal else None
+
+    if args.copy_calibration:
+        src = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    holder = {}
+
+    def s_fwd_bwd():
+        holder["out"] = standard_attention(q, k, v, do, w.scale, mask)
+
+    def nothing():
+        pass
+
+    f_fwd, f_bwd = convention_flops(w, 0)
+    res = {}
+    ms, fm, bm = _time_fwd_bwd(t_fwd, t_bwd, args.steps, args.warmup, stream)
+    res["tiled"] = {"ms_per_step": round(ms, 5), "fwd_ms": round(fm, 5), "bwd_ms": round(bm, 5)}
+    # the standard chain is one function; time it whole (events bracket it)
+    ms_s, _, _ = _time_fwd_bwd(s_fwd_bwd, nothing, args.steps, args.warmup, stream)
+    res["standard"] = {"ms_per_step": round(ms_s, 5)}
+    holder.clear()
+    for name, r in res.items():
+        r["tflops"] = round((f_fwd + f_bwd) / (r["ms_per_step"] * 1e-3) / 1e12, 3)
+    del o, lse, dq, dk, dv, ws
+    res["tiled"]["peak_extra_bytes"] = _peak_extra_bytes(
+        lambda: (fa.backward(q, k, v, *fa.forward(q, k, v, scale=w.scale, causal=w.causal), do,
+                             scale=w.scale, causal=w.causal)))
+    res["standard"]["peak_extra_bytes"] = _peak_extra_bytes(lambda: standard_attention(q, k, v, do, w.scale, mask))
+    traffic = read_step_traffic(w.name)
+    for name in res:
+        res[name]["hbm_bytes_per_step"] = traffic.get(name)
+    line = {
+        "metric": "standard vs tiled attention, fwd+bwd on 1 MI355X",
+        "workload": f"{w.name}: {WORKLOAD_TEXT[w.name]}",
+        "dtype": DTYPE_NAME[w.dtype],
+        "data": "synthetic",
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "convention_gflop_per_step": round((f_fwd + f_bwd) / 1e9, 3),
+        "standard_computes": "full N x N products (the causal mask is applied after the GEMM); "
+                             "outputs and gradients in the input dtype",
+        "tiled": res["tiled"],
+        "standard": res["standard"],
+        "speedup": round(res["standard"]["ms_per_step"] / res["tiled"]["ms_per_step"], 3),
+    }
+    if traffic.get("standard") and traffic.get("tiled"):
+        line["hbm_ratio"] = round(traffic["standard"] / traffic["tiled"], 3)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_sweep(args):
+    """Tiled attention (bf16, causal) over sequence lengths: fwd and fwd+bwd
+    time, convention TFLOP/s and peak extra device memory, with standard
+    attention beside it while its N x N intermediates fit the memory cap."""
+    import torch
+
+    import io_aware_exact_14_amd as fa
+    from io_aware_exact_14_amd import _lib
+    from workloads import draw_qkvdo
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    lib = _lib.load()
+    rows = []
+    for d in [int(t) for t in args.sweep_d.split(",")]:
+        H = 1024 // d
+        for N in [int(t) for t in args.sweep_n.split(",")]:
+            B = max(1, args.sweep_tokens // N)
+            q, k, v, do = (t.to(dev) for t in draw_qkvdo(B, H, N, d, torch.bfloat16, 4000 + N + d))
+            scale = 1.0 / math.sqrt(d)
+            p = fa.params(B, H, N, d, torch.bfloat16, scale=scale, causal=True)
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+            dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+            ws = torch.empty(max(int(lib.fa_bwd_workspace_bytes(ctypes.byref(p))), 1), dtype=torch.uint8,
+                             device=dev)
+            t_fwd, t_bwd = _tiled_step_fn(lib, p, q, k, v, do, o, lse, dq, dk, dv, ws, stream)
+            steps = max(3, min(args.steps, int(2e5 // N)))
+            ms, fm, bm = _time_fwd_bwd(t_fwd, t_bwd, steps, max(1, min(args.warmup, 3)), stream)
+            fwd_fl = 4.0 * B * H * N * N * d * 0.5
+            del o, lse, dq, dk, dv, ws
+            row = {"N": N, "B": B, "H": H, "d": d, "steps": steps,
+                   "tiled": {"ms_per_step": round(ms, 4), "fwd_ms": round(fm, 4), "bwd_ms": round(bm, 4),
+                             "fwd_tflops": round(fwd_fl / (fm * 1e-3) / 1e12, 2),
+                             "bwd_tflops": round(2.5 * fwd_fl / (bm * 1e-3) / 1e12, 2),
+                             "tflops": round(3.5 * fwd_fl / (ms * 1e-3) / 1e12, 2),
+                             "peak_extra_bytes": _peak_extra_bytes(
+                                 lambda: fa.backward(q, k, v, *fa.forward(q, k, v, causal=True), do,
+                                                     causal=True))}}
+            # standard attention peaks at four live N x N matrices (measured)
+            need = 4 * B * H * N * N * 2
+            if need <= args.standard_cap_gb * 2**30:
+                mask = torch.ones(N, N, dtype=torch.bool).triu_(1).to(dev)
+                holder = {}
+
+                def s_run():
+                    holder["o"] = standard_attention(q, k, v, do, scale, mask)
+
+                sms, _, _ = _time_fwd_bwd(s_run, lambda: None, max(2, steps // 2), 1, stream)
+                holder.clear()
+                row["standard"] = {"ms_per_step": round(sms, 4),
+                                   "tflops": round(3.5 * fwd_fl / (sms * 1e-3) / 1e12, 2),
+                                   "peak_extra_bytes": _peak_extra_bytes(
+                                       lambda: standard_attention(q, k, v, do, scale, mask))}
+                del mask
+            else:
+                row["standard"] = {"skipped": f"four N x N matrices need {need / 2**30:.0f} GiB, above the "
+                                              f"{args.standard_cap_gb} GiB cap"}
+            print(json.dumps(row), file=sys.stderr, flush=True)
+            rows.append(row)
+            del q, k, v, do
+            torch.cuda.empty_cache()
+    print(json.dumps({"metric": "tiled attention fwd+bwd over sequence length on 1 MI355X (bf16, causal, "
+                                "hidden 1024)", "data": "synthetic", "unit": "TFLOP/s", "rows": rows}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +435,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 512 MiB device copy first (reference kernel for HBM counters)")
+    ap.add_argument("--standard", action="store_true", help="standard vs tiled attention on --workload")
+    ap.add_argument("--sweep", action="store_true", help="sequence-length sweep of the tiled kernels")
+    ap.add_argument("--sweep-n", default="1024,2048,4096,8192,16384,32768,65536")
+    ap.add_argument("--sweep-d", default="64,128")
+    ap.add_argument("--sweep-tokens", type=int, default=16384, help="B = max(1, tokens // N)")
+    ap.add_argument("--standard-cap-gb", type=float, default=64.0)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -160,6 +448,10 @@ def main():
         print("bench.py measures one GPU only: the attention path here is single-GPU "
               "(heads would shard over GPUs with no communication); run with --gpus 1", file=sys.stderr)
         return 2
+    if args.standard:
+        return run_standard(args)
+    if args.sweep:
+        return run_sweep(args)
 
     import numpy as np
     import torch
