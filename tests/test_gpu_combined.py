@@ -1,0 +1,65 @@
+"""GPU parity with every option combined: causal and block-sparse masking and
+dropout together, odd batch and head counts, a ragged sequence length, a
+non-default softmax scale (0.3, logits of std ~2.4 at d = 64) and both
+gradient precisions, forward and backward, against the fp64 oracle.
+
+Errors grow with the size of the gradients (peaky rows, 1/(1-p) scaling; at
+p = 0.9 and scale 0.3 |dK| reaches 85). For 16-bit inputs they come from the
+rounding of P and dS to the input dtype before the second products; for fp32
+inputs from fp32 arithmetic. So the bound here is the larger of the fixed
+bound (1e-4 fp32, 2e-2 16-bit) and twice the error of the textbook algorithm
+run in the same precision on the same inputs (tests/_lowp_ref.py)."""
+import numpy as np
+import pytest
+import torch
+
+from tests._gpu import TOL, inputs, max_abs, note, oracle_bwd, oracle_fwd, to_dev
+from tests._lowp_ref import lowp_attention
+from workloads import random_block_mask
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # dtype, d, N, mask_block, dropout p, gradient dtype ("fp32" or "input")
+    (torch.bfloat16, 64, 777, 128, 0.15, "fp32"),
+    (torch.float16, 64, 777, 256, 0.3, "fp32"),
+    (torch.bfloat16, 128, 530, 128, 0.1, "input"),
+    (torch.float16, 128, 300, 128, 0.9, "fp32"),
+    (torch.float32, 64, 333, 128, 0.2, "fp32"),
+    (torch.float32, 128, 400, 128, 0.9, "fp32"),
+]
+
+
+@pytest.mark.parametrize("dtype,d,N,mb,p,gd", CASES,
+                         ids=[f"{str(c[0])[6:]}-d{c[1]}-N{c[2]}-mb{c[3]}-p{c[4]}-{c[5]}" for c in CASES])
+def test_all_options_combined(fa, dtype, d, N, mb, p, gd):
+    B, H, scale, seed = 3, 5, 0.3, 0xC0FFEE123
+    nb = (N + mb - 1) // mb
+    # no forced diagonal: some row blocks end up with no visible key at all
+    bm = random_block_mask(nb, seed=N + d, frac=0.5, keep_diag=False)
+    note(f"combined B={B} H={H} N={N} d={d} {dtype} mb={mb} p={p} grads={gd}")
+    q, k, v, do = inputs(B, H, N, d, dtype, N + 17)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    kw = dict(scale=scale, causal=True, dropout_p=p, seed=seed, block_mask=torch.from_numpy(bm), mask_block=mb)
+    o, lse = fa.forward(qd, kd, vd, **kw)
+    grad_dtype = torch.float32 if gd == "fp32" else dtype
+    dq, dk, dv = fa.backward(qd, kd, vd, o, lse, dod, grad_dtype=grad_dtype, **kw)
+    torch.cuda.synchronize()
+    O, L = oracle_fwd(q, k, v, scale, True, p, seed, bm, mb)
+    G = oracle_bwd(q, k, v, do, scale, True, p, seed, bm, mb)
+    errs = {"O": max_abs(o.float().cpu().numpy(), O), "LSE": max_abs(lse.cpu().numpy(), L)}
+    for name, got, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), G):
+        assert got.dtype == grad_dtype
+        errs[name] = max_abs(got.float().cpu().numpy(), ref)
+    tol = {n: TOL[dtype] for n in errs}
+    lowp = lowp_attention(q, k, v, do, scale, True, p, seed, bm, mb)
+    for name, r, ref in zip(("O", "dQ", "dK", "dV"), lowp, (O,) + tuple(G)):
+        tol[name] = max(TOL[dtype], 2.0 * max_abs(r, ref))
+    assert all(errs[n] <= tol[n] for n in errs), (errs, tol)
+    # rows whose every block is masked produce O = 0, LSE = -inf and zero dQ
+    empty = ~(bm.astype(bool) & np.tril(np.ones((nb, nb), bool))).any(axis=1)
+    if empty.any():
+        rows = np.concatenate([np.arange(r * mb, min(N, (r + 1) * mb)) for r in np.nonzero(empty)[0]])
+        assert np.all(np.isneginf(lse.cpu().numpy()[:, :, rows]))
+        assert np.all(o.float().cpu().numpy()[:, :, rows] == 0)
+        assert np.all(dq.float().cpu().numpy()[:, :, rows] == 0)
