@@ -92,7 +92,10 @@ int fa_fwd(const fa_params* p, const void* Q, const void* K, const void* V, void
   a.v = V;
   a.out = O;
   a.lse = LSE;
-  const hipError_t e = fa::launch_fwd(elt(p->in_dtype), (int)p->d, a.thresh != 0, a, (hipStream_t)stream);
+  // Any p > 0 takes the dropout kernels, even when floor(p * 2^32) is 0 and
+  // every element is kept: the output is still scaled by 1 / (1 - p).
+  const bool dropout = p->dropout_p > 0.0;
+  const hipError_t e = fa::launch_fwd(elt(p->in_dtype), (int)p->d, dropout, a, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -132,8 +135,8 @@ int bwd_stage(int stage, const fa_params* p, const void* Q, const void* K, const
   a.dk = dK;
   a.dv = dV;
   a.delta = static_cast<float*>(workspace);
-  const hipError_t e = fa::launch_bwd(elt(p->in_dtype), elt(p->grad_dtype), (int)p->d, a.thresh != 0, stage, a,
-                                      (hipStream_t)stream);
+  const hipError_t e = fa::launch_bwd(elt(p->in_dtype), elt(p->grad_dtype), (int)p->d, p->dropout_p > 0.0, stage,
+                                      a, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
