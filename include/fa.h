@@ -68,7 +68,7 @@ typedef enum {
   FA_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than fa_bwd_workspace_bytes */
   FA_ERR_HIP = 9,         /* the HIP runtime reported an error at launch */
   FA_ERR_SCALE = 10,      /* scale not finite and > 0 */
-  FA_ERR_RANGE = 11       /* fa_dropout_mask window outside [0, N) */
+  FA_ERR_RANGE = 11       /* fa_dropout_mask window, (b, h) or size out of range */
 } fa_status;
 
 typedef struct {
@@ -135,7 +135,9 @@ int fa_bwd_dkdv(const fa_params* p, const void* Q, const void* K, const void* V,
  * [i0, i0+rows) and key columns [j0, j0+cols) into the DEVICE buffer
  * keep[rows][cols], with the same device function the fused kernels use.
  * Masking (causal, block mask) is not applied. With dropout_p == 0 every bit
- * is 1.
+ * is 1. The window must lie inside [0, N) x [0, N), (b, h) inside
+ * [0, B) x [0, H), and rows * cols must stay below 2^39; otherwise the call
+ * returns FA_ERR_RANGE.
  */
 int fa_dropout_mask(const fa_params* p, int64_t b, int64_t h, int64_t i0, int64_t rows,
                     int64_t j0, int64_t cols, uint8_t* keep, void* stream);
