@@ -507,7 +507,7 @@ static hipError_t launch_bwd_cfg(int stage, const AttnArgs& a, hipStream_t s) {
     if constexpr (!h)
       e = launch_dq<T, G, D, DROP, D == 64 ? 64 : 32, 1>(a, s);
     else if constexpr (D == 128)
-      e = launch_dq<T, G, D, DROP, 64, DROP ? 1 : 2>(a, s);
+      e = launch_dq<T, G, D, DROP, 64, 2>(a, s);
     else
       e = a.N <= 4096 ? launch_dq<T, G, D, DROP, 32, DROP ? 2 : 3>(a, s) : launch_dq<T, G, D, DROP, 64, 2>(a, s);
     if (e != hipSuccess) return e;

@@ -198,6 +198,10 @@ __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int voff
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, 0, 0);
 }
 
+// This lane's index in its wave (0..63), recomputed from the execution mask
+// counters rather than kept in a register across a loop.
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
 // True if `pred` holds in any lane of the wave.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

@@ -210,7 +210,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         if (need_mask) {
           // Hide keys past min(q, N-1) (causal) or past N-1; key - k0 is a
           // compile-time offset plus 4*hi, so each element costs one compare.
-          const int t = (a.causal ? min(qb_[b], N - 1) : N - 1) - k0 - 4 * hi;
+          // The lane terms are recomputed here (q0b is wave-uniform), which
+          // keeps them out of the registers live across the tile loop.
+          const int ln = lane_id();
+          const int t = (a.causal ? min(q0b[b] + (ln & 31), N - 1) : N - 1) - k0 - 4 * (ln >> 5);
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
