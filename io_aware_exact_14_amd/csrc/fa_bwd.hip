@@ -304,9 +304,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   auto kept = [&](int i) {
     return a.bmask == nullptr || mask_kept(a.bmask, ((i * BR) / a.mask_block) * a.nb + cblk);
   };
-  auto next_kept = [&](int i) {
-    ++i;
-    while (i < nqt && !kept(i)) ++i;
+  // Query tiles run from the end of the sequence down to the diagonal: every
+  // key block of a head then reads the same Q/dO tile at the same iteration,
+  // so the workgroups of a head running together share it through L2.
+  auto prev_kept = [&](int i) {
+    --i;
+    while (i >= istart && !kept(i)) --i;
     return i;
   };
 
@@ -354,17 +357,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     dv[db] = zero16();
   }
 
-  int it = istart < nqt && kept(istart) ? istart : next_kept(istart);
+  int it = nqt - 1 >= istart && kept(nqt - 1) ? nqt - 1 : prev_kept(nqt - 1);
   int cur = 0;
-  if (it < nqt) {
+  if (it >= istart) {
     gload(it);
     sstore(0);
   }
   __syncthreads();
 
-  while (it < nqt) {
-    const int itn = next_kept(it);
-    gload(itn < nqt ? itn : it);  // unconditional prefetch (see the forward kernel)
+  while (it >= istart) {
+    const int itn = prev_kept(it);
+    gload(itn >= istart ? itn : it);  // unconditional prefetch (see the forward kernel)
     const T* Qs = &smem[cur][0];
     const T* dOs = &smem[cur][TILE];
     const int i0 = it * BR;
