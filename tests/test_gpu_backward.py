@@ -150,3 +150,23 @@ def test_keep_bits_used_inside_backward(fa, p):
 def test_backward_long_rows(fa, N, causal, p):
     # longer sequences take the large-tile launch configurations (with tails)
     _check_bwd(fa, 1, 1, N, 64, torch.bfloat16, causal=causal, p=p, seed=0x5EED0003, in_seed=N + 5)
+
+
+def test_side_stream_gives_identical_results(fa):
+    # every call enqueues on the caller's current stream; the library keeps
+    # no state, so a side stream yields the same bits as the default stream
+    q, k, v, do = inputs(2, 3, 300, 64, torch.bfloat16, 41)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    kw = dict(causal=True, dropout_p=0.1, seed=11)
+    note("side stream fwd+bwd")
+    o1, l1 = fa.forward(qd, kd, vd, **kw)
+    g1 = fa.backward(qd, kd, vd, o1, l1, dod, **kw)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o2, l2 = fa.forward(qd, kd, vd, **kw)
+        g2 = fa.backward(qd, kd, vd, o2, l2, dod, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for a, b in zip((o1, l1) + tuple(g1), (o2, l2) + tuple(g2)):
+        assert torch.equal(a, b)
