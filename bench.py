@@ -435,6 +435,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 512 MiB device copy first (reference kernel for HBM counters)")
+    ap.add_argument("--flush", action="store_true",
+                    help="also time K steps with a 512 MiB write before each, so no input is cached")
     ap.add_argument("--standard", action="store_true", help="standard vs tiled attention on --workload")
     ap.add_argument("--sweep", action="store_true", help="sequence-length sweep of the tiled kernels")
     ap.add_argument("--sweep-n", default="1024,2048,4096,8192,16384,32768,65536")
@@ -536,6 +538,23 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     kdur = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
+
+    flushed = None
+    if args.flush:
+        # Cold caches: a 512 MiB write (twice the 256 MB last-level cache)
+        # before every step, kept outside the HIP events around the kernels.
+        junk = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            junk.fill_(float(i))
+            step(fev[i])
+        torch.cuda.synchronize()
+        del junk
+        fdur = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in fev) / args.steps for j, n in enumerate(names)}
+        flushed = {"ms_per_step": round(sum(fdur.values()), 5),
+                   "per_kernel_ms": {n: round(fdur[n], 5) for n in names},
+                   "tflops": round((convention_flops(w, kept)[0] + convention_flops(w, kept)[1])
+                                   / (sum(fdur.values()) * 1e-3) / 1e12, 3)}
     f_fwd, f_bwd = convention_flops(w, kept)
     value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
 
@@ -579,6 +598,8 @@ def main():
                    "seq_len": w.N, "head_dim": w.d, "grad_dtype": "fp32", "parallelism": "none (1 GPU)"},
         "roofline": roof,
     }
+    if flushed is not None:
+        result["flushed"] = flushed
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(result), flush=True)
