@@ -35,10 +35,13 @@ template <typename T, int D, int BC, int QB>
 struct FwdCfg {
   static constexpr int BR = 128 * QB;                       // queries per workgroup (4 waves x 32 x QB)
   static constexpr int EPC = 16 / sizeof(T);                // elements per 16-byte chunk
-  // K/V tile row stride (elements). 16-bit rows are padded so that transpose reads
-  // (ds_read_b64_tr_b16) stay free of bank conflicts: 144 B at d = 64 and 288 B
-  // at d = 128; a 272 B stride measured 124 against 193 B/clk per CU.
-  static constexpr int KS = D + (sizeof(T) == 2 ? (D == 128 ? 16 : 8) : 4);
+  // K/V tile row stride (elements). 16-bit rows are padded so that both fragment
+  // patterns avoid bank conflicts: 16-byte row reads need a stride of 4 mod 8
+  // dwords (the 16 rows a 16-lane group reads then land on distinct bank
+  // quads), and transpose reads (ds_read_b64_tr_b16) measured 124 B/clk per CU
+  // at 272 B against 193 at 144, 288 or 304 B. So 144 B at d = 64 and 304 B at
+  // d = 128 (288 B left the row reads 2-way conflicted: +4-8% time).
+  static constexpr int KS = D + (sizeof(T) == 2 ? (D == 128 ? 24 : 8) : 4);
   static constexpr int KCH = D / EPC;                       // 16-byte chunks per K/V row
   static constexpr int NLD = BC * KCH / 256;                // 16-byte loads per lane per tensor per tile
   static constexpr int TILE = BC * KS;                      // elements per K (or V) tile
