@@ -76,14 +76,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lo = lane & 31, hi = lane >> 5;
 
-  // Workgroups are numbered tile-major: consecutive ids are different heads
-  // of the same query tile, so with B*H a multiple of 8 all tiles of a head
-  // land on the same XCD (ids are dealt round-robin over the 8 XCDs) and
-  // share its L2. Causal: longest rows first.
+  // Causal: longest rows first; a grid that fits the 256 CUs at WPE
+  // workgroups each balances their loads (tile_order).
   const int N = a.N;
   const int nq = (N + C::BR - 1) / C::BR;
-  const int rank = blockIdx.x / a.BH;
-  const int bh = blockIdx.x - rank * a.BH;
+  int rank, bh;
+  tile_order((int)blockIdx.x, nq, a.BH, a.causal && nq * a.BH <= 256 * WPE, rank, bh);
   const int qt = a.causal ? (nq - 1 - rank) : rank;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const T* __restrict__ Kg = static_cast<const T*>(a.k) + hoff;
