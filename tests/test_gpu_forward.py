@@ -43,6 +43,17 @@ def test_forward_tails_and_multiple_tiles(fa, N):
     _check_fwd(fa, 1, 3, N, 128, torch.bfloat16, causal=False, in_seed=N + 2)
 
 
+@pytest.mark.parametrize("B,H,N,d,dtype", [
+    (1, 8, 4001, 64, torch.bfloat16),   # 32 tiles x 8 heads, 4 workgroups per CU, ragged tail
+    (2, 8, 2000, 64, torch.float32),    # 16 tiles x 16 heads, 2 workgroups per CU
+    (1, 8, 4001, 128, torch.float16),   # 32 tiles x 8 heads, 2 workgroups per CU
+])
+def test_forward_causal_grids_resident_at_once(fa, B, H, N, d, dtype):
+    # causal grids that fit the chip in one round take the balanced
+    # (serpentine) tile order; every head is checked whole
+    _check_fwd(fa, B, H, N, d, dtype, causal=True, in_seed=N + d)
+
+
 def test_forward_workload_c1_fp32(fa):
     # single-head, non-causal, fp32, N=128, d=64 at its full size
     from workloads import WORKLOADS, workload_inputs
