@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   uint32_t rowhash = 0;
   if constexpr (DROP) {
     const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
-    rowhash = fmix32(hk ^ (uint32_t)q);
+    rowhash = fmix32(hk ^ (uint32_t)q) ^ (uint32_t)(4 * hi);  // crow's 4*hi folded in (fmix32_head)
   }
 
   const int kend = a.causal ? min(N, qtile0 + BR) : N;
@@ -181,17 +181,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
           for (int v = 0; v < 16; ++v)
             if (kb * 32 + 8 * (v >> 2) + (v & 3) > t) s[kb][v] = NEG_INF;
       }
+      const uint32_t y = fmix32_head(rowhash ^ (uint32_t)k0);  // keys k0 | offset below BC
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = exp2_fast(fmaf(s[kb][v], a.sl2, -lse2));
-          float dpv = dp[kb][v];
-          if constexpr (DROP) {
-            const uint32_t key = (uint32_t)(k0 + kb * 32 + crow(v, hi));
-            dpv = fmix32(rowhash ^ key) >= a.thresh ? dpv * a.rp : 0.f;
+          float ds = dp[kb][v] - Dq;
+          if constexpr (DROP) {  // dP * Z / (1 - p) - D
+            const uint32_t off = (uint32_t)(kb * 32 + 8 * (v >> 2) + (v & 3));
+            ds = fmix32_tail(y ^ off) >= a.thresh ? fmaf(dp[kb][v], a.rp, -Dq) : -Dq;
           }
-          s[kb][v] = p * (dpv - Dq);  // dS^T
+          s[kb][v] = p * ds;  // dS^T
         }
       if constexpr (KH == 8) {
 #pragma unroll
@@ -276,6 +277,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int k0w = k0wg + w * 32;
   const int key = k0w + lo;
   const bool kvalid = key < N;
+  const uint32_t keyh = fmix32_head((uint32_t)key);  // the row words in LDS carry their head step too
 
   // Keys past the end are clamped to row N-1: their scores are masked and
   // their gradients never stored.
@@ -336,7 +338,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const float l = Lg[qic];
     l_reg = (qi >= N || l == NEG_INF) ? POS_INF : l * kLog2e;
     d_reg = Dg[qic];
-    if constexpr (DROP) h_reg = fmix32(hk ^ (uint32_t)qi);
+    if constexpr (DROP) h_reg = fmix32_head(fmix32(hk ^ (uint32_t)qi));  // head step of the (row, key) hash
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -420,14 +422,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * g + e;
             const float p = exp2_fast(fmaf(s[qb][v], a.sl2, -l4[e]));
-            float pd = p, dpv = dp[qb][v];
+            float pd = p, ds = dp[qb][v] - d4[e];
             if constexpr (DROP) {
-              const bool keep = fmix32(h4[e] ^ (uint32_t)key) >= a.thresh;
-              pd = keep ? p * a.rp : 0.f;
-              dpv = keep ? dpv * a.rp : 0.f;
+              const bool keep = fmix32_tail(h4[e] ^ keyh) >= a.thresh;
+              pd = keep ? p : 0.f;                                // 1 / (1 - p) goes on dV at the end
+              ds = keep ? fmaf(dp[qb][v], a.rp, -d4[e]) : -d4[e];  // dP * Z / (1 - p) - D
             }
-            s[qb][v] = pd;                    // P * Z / (1 - p)
-            dp[qb][v] = p * (dpv - d4[e]);    // dS
+            s[qb][v] = pd;       // P * Z
+            dp[qb][v] = p * ds;  // dS
           }
         }
       if constexpr (KH == 8) {
@@ -468,6 +470,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 
   if (kvalid) {
     const float sc = a.scale;
+    const float sv = DROP ? a.rp : 1.f;  // dV = sum_i (P * Z)_ij dO_i / (1 - p)
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -475,7 +478,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         const int off = key * D + db * 32 + 8 * g + 4 * hi;
         store4<G>(dKg + off, dk[db][4 * g] * sc, dk[db][4 * g + 1] * sc, dk[db][4 * g + 2] * sc,
                   dk[db][4 * g + 3] * sc);
-        store4<G>(dVg + off, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+        store4<G>(dVg + off, dv[db][4 * g] * sv, dv[db][4 * g + 1] * sv, dv[db][4 * g + 2] * sv,
+                  dv[db][4 * g + 3] * sv);
       }
   }
 }

@@ -119,15 +119,21 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ float half_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float half_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
-// MurmurHash3 32-bit finalizer (Appleby, public domain).
-__device__ __forceinline__ uint32_t fmix32(uint32_t x) {
-  x ^= x >> 16;
+// MurmurHash3 32-bit finalizer (Appleby, public domain), split after its
+// first step. That step is linear over XOR, fmix32_head(a ^ b) =
+// fmix32_head(a) ^ fmix32_head(b), and leaves b < 2^16 unchanged, so the keep
+// hash of a row word r and the key k0 | off (off < 2^16) is
+// fmix32_tail(fmix32_head(r ^ k0) ^ off): one word per tile, then one XOR per
+// key.
+__device__ __forceinline__ uint32_t fmix32_head(uint32_t x) { return x ^ (x >> 16); }
+__device__ __forceinline__ uint32_t fmix32_tail(uint32_t x) {
   x *= 0x85EBCA6Bu;
   x ^= x >> 13;
   x *= 0xC2B2AE35u;
   x ^= x >> 16;
   return x;
 }
+__device__ __forceinline__ uint32_t fmix32(uint32_t x) { return fmix32_tail(fmix32_head(x)); }
 
 // Per-(b, h) dropout key from the 64-bit seed.
 __device__ __forceinline__ uint32_t head_key(uint32_t seed_lo, uint32_t seed_hi, uint32_t b, uint32_t h) {
