@@ -99,6 +99,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const float lraw = a.lse[(size_t)bh * N + qc];
   const float lse2 = (!qvalid || lraw == NEG_INF) ? POS_INF : lraw * kLog2e;
   if (qvalid && hi == 0) a.delta[(size_t)bh * N + q] = Dq;
+  // Without dropout the dP products start from -D of this lane's query. The
+  // 16 registers are spent only on the 64-key tiles at d = 64: the 32-key
+  // kernel fits 128 VGPRs without them, which lets four waves share a SIMD.
+  constexpr bool kNegD = !DROP && D == 64 && BC == 64;
+  f32x16 negd;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) negd[v] = -Dq;
   uint32_t rowhash = 0;
   if constexpr (DROP) {
     const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
@@ -161,7 +168,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = zero16();
-        dp[kb] = zero16();
+        dp[kb] = kNegD ? negd : zero16();  // from -D the product yields dP - D directly
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -187,7 +194,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = exp2_fast(fmaf(s[kb][v], a.sl2, -lse2));
-          float ds = dp[kb][v] - Dq;
+          float ds = kNegD ? dp[kb][v] : dp[kb][v] - Dq;
           if constexpr (DROP) {  // dP * Z / (1 - p) - D
             const uint32_t off = (uint32_t)(kb * 32 + 8 * (v >> 2) + (v & 3));
             ds = fmix32_tail(y ^ off) >= a.thresh ? fmaf(dp[kb][v], a.rp, -Dq) : -Dq;
@@ -253,7 +260,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 
   __shared__ __attribute__((aligned(16))) T smem[2][2 * TILE];  // [buffer][Q tile | dO tile]
   __shared__ __attribute__((aligned(16))) float side_l[2][BR];  // LSE in log2 units (+inf: no valid key)
-  __shared__ __attribute__((aligned(16))) float side_d[2][BR];  // D_i
+  __shared__ __attribute__((aligned(16))) float side_d[2][BR];  // -D_i
   __shared__ __attribute__((aligned(16))) uint32_t side_h[2][BR];  // dropout row hash
   __shared__ __attribute__((aligned(16))) T vsm[VLDS ? BK * S::KS : 8];  // V rows of this workgroup
 
@@ -337,7 +344,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const int qic = min(qi, N - 1);
     const float l = Lg[qic];
     l_reg = (qi >= N || l == NEG_INF) ? POS_INF : l * kLog2e;
-    d_reg = Dg[qic];
+    d_reg = -Dg[qic];
     if constexpr (DROP) h_reg = fmix32_head(fmix32(hk ^ (uint32_t)qi));  // head step of the (row, key) hash
   };
   auto sstore = [&](int buf) {
@@ -383,7 +390,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         s[qb] = zero16();
-        dp[qb] = zero16();
+        if constexpr (DROP) {
+          dp[qb] = zero16();
+        } else {
+          // Start the product from -D of each element's query: it then yields dP - D.
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&side_d[cur][qb * 32 + 8 * g + 4 * hi]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[qb][4 * g + e] = d4[e];
+          }
+        }
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -415,18 +432,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int g = 0; g < 4; ++g) {
           const int ql = qb * 32 + 8 * g + 4 * hi;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&side_l[cur][ql]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&side_d[cur][ql]);
+          f32x4 nd4 = {0.f, 0.f, 0.f, 0.f};  // -D
           u32x4 h4 = {0, 0, 0, 0};
-          if constexpr (DROP) h4 = *reinterpret_cast<const u32x4*>(&side_h[cur][ql]);
+          if constexpr (DROP) {
+            nd4 = *reinterpret_cast<const f32x4*>(&side_d[cur][ql]);
+            h4 = *reinterpret_cast<const u32x4*>(&side_h[cur][ql]);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * g + e;
             const float p = exp2_fast(fmaf(s[qb][v], a.sl2, -l4[e]));
-            float pd = p, ds = dp[qb][v] - d4[e];
+            float pd = p, ds = dp[qb][v];  // dP - D
             if constexpr (DROP) {
               const bool keep = fmix32_tail(h4[e] ^ keyh) >= a.thresh;
               pd = keep ? p : 0.f;                                // 1 / (1 - p) goes on dV at the end
-              ds = keep ? fmaf(dp[qb][v], a.rp, -d4[e]) : -d4[e];  // dP * Z / (1 - p) - D
+              ds = keep ? fmaf(dp[qb][v], a.rp, nd4[e]) : nd4[e];  // dP * Z / (1 - p) - D
             }
             s[qb][v] = pd;       // P * Z
             dp[qb][v] = p * ds;  // dS
