@@ -54,6 +54,11 @@ def test_forward_causal_grids_resident_at_once(fa, B, H, N, d, dtype):
     _check_fwd(fa, B, H, N, d, dtype, causal=True, in_seed=N + d)
 
 
+def test_forward_causal_grid_resident_at_once_with_dropout(fa):
+    # dropout indexes by (b, h, query, key), whatever workgroup computes the tile
+    _check_fwd(fa, 1, 8, 4001, 64, torch.bfloat16, causal=True, p=0.2, seed=77, in_seed=9)
+
+
 def test_forward_workload_c1_fp32(fa):
     # single-head, non-causal, fp32, N=128, d=64 at its full size
     from workloads import WORKLOADS, workload_inputs
