@@ -44,6 +44,12 @@ def test_backward_tails_and_multiple_tiles(fa, N):
     _check_bwd(fa, 1, 2, N, 128, torch.bfloat16, causal=False, in_seed=N + 1)
 
 
+def test_backward_causal_sixteen_heads_ragged(fa):
+    # 16 query tiles x 16 heads (ragged last tile): a causal grid that fits
+    # the chip in one round; every head checked whole
+    _check_bwd(fa, 1, 16, 2001, 64, torch.bfloat16, causal=True, in_seed=21)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("d", [64, 128])
 def test_backward_dropout(fa, dtype, d):
