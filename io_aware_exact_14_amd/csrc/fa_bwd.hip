@@ -229,8 +229,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     j = jn;
   }
 
-  if (qvalid) {
-    const float sc = a.scale;
+  const float sc = a.scale;
+  if constexpr (D == 64 && sizeof(T) == 2) {
+    // Staged through LDS as in the dK/dV kernel, one 32-column half at a
+    // time (four waves' halves fit the tile buffers): each store then writes
+    // 128 contiguous bytes of 8 rows. Row stride 36 floats: 16 consecutive
+    // rows start on distinct bank quads.
+    constexpr int RS = 32 + 4;
+    constexpr int WAVE_FLOATS = 32 * RS;
+    static_assert(sizeof(smem) >= 4 * WAVE_FLOATS * sizeof(float), "staging space in the tile buffers");
+    float* st = reinterpret_cast<float*>(&smem[0][0]) + w * WAVE_FLOATS;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = {dq[db][4 * g] * sc, dq[db][4 * g + 1] * sc, dq[db][4 * g + 2] * sc, dq[db][4 * g + 3] * sc};
+        *reinterpret_cast<f32x4*>(&st[lo * RS + 8 * g + 4 * hi]) = x;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // 32 rows x 8 pieces of 4 values, 64 lanes
+        const int c = i * 64 + lane;
+        const int row = c >> 3, ch = c & 7;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&st[row * RS + ch * 4]);
+        if (q0w + row < N) store4<G>(dQg + (q0w + row) * D + db * 32 + ch * 4, x[0], x[1], x[2], x[3]);
+      }
+      __syncthreads();  // the area is reused for the next half
+    }
+  } else if (qvalid) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -488,9 +514,46 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     it = itn;
   }
 
-  if (kvalid) {
-    const float sc = a.scale;
-    const float sv = DROP ? a.rp : 1.f;  // dV = sum_i (P * Z)_ij dO_i / (1 - p)
+  const float sc = a.scale;
+  const float sv = DROP ? a.rp : 1.f;  // dV = sum_i (P * Z)_ij dO_i / (1 - p)
+  if constexpr (D == 64 && sizeof(T) == 2) {
+    // A lane holds 4-value pieces of 32 rows, so a direct store writes 32
+    // bytes to each of 32 rows. Each wave instead stages its 32 rows in LDS
+    // (the tile buffers are free now) and stores four whole rows per
+    // instruction. Row stride 68 floats: the pieces of 16 rows land on
+    // distinct bank quads.
+    constexpr int RS = D + 4;
+    constexpr int WAVE_FLOATS = 32 * RS;
+    static_assert(sizeof(smem) >= (VLDS ? 2 : 4) * WAVE_FLOATS * sizeof(float), "staging space in the tile buffers");
+    static_assert(!VLDS || sizeof(vsm) >= 2 * WAVE_FLOATS * sizeof(float), "staging space in the V rows");
+    float* st;
+    if constexpr (VLDS)
+      st = (w < 2 ? reinterpret_cast<float*>(&smem[0][0]) : reinterpret_cast<float*>(&vsm[0])) + (w & 1) * WAVE_FLOATS;
+    else
+      st = reinterpret_cast<float*>(&smem[0][0]) + w * WAVE_FLOATS;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const f32x16* acc = t == 0 ? dk : dv;
+      const float f = t == 0 ? sc : sv;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = {acc[db][4 * g] * f, acc[db][4 * g + 1] * f, acc[db][4 * g + 2] * f, acc[db][4 * g + 3] * f};
+          *reinterpret_cast<f32x4*>(&st[lo * RS + db * 32 + 8 * g + 4 * hi]) = x;
+        }
+      __syncthreads();
+      G* __restrict__ dst = t == 0 ? dKg : dVg;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {  // 32 rows x 16 pieces of 4 values, 64 lanes
+        const int c = i * 64 + lane;
+        const int row = c >> 4, ch = c & 15;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&st[row * RS + ch * 4]);
+        if (k0w + row < N) store4<G>(dst + (k0w + row) * D + ch * 4, x[0], x[1], x[2], x[3]);
+      }
+      __syncthreads();  // the area is reused for dV
+    }
+  } else if (kvalid) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
