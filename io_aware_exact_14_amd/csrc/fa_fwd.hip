@@ -307,6 +307,39 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 
   const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(static_cast<T*>(a.out) + hoff, N * RB);
   const __amdgpu_buffer_rsrc_t lrs = buffer_rsrc(a.lse + (size_t)bh * N, N * 4);
+  if constexpr (D == 64 && QB == 1 && sizeof(T) == 2) {
+    // A lane holds 4-value pieces of its row, so a direct store writes 8
+    // bytes to each of 32 rows. Each wave instead stages its 32 rows in the
+    // tile buffers (free after the loop's last barrier) and stores 8 whole
+    // rows per instruction; rows past the end fall outside the buffer
+    // resource and are dropped. Row stride 72 elements (144 bytes): 16
+    // consecutive rows start on distinct bank quads.
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    constexpr int RSE = D + 8;
+    constexpr int WAVE_ELTS = 32 * RSE;
+    static_assert(sizeof(smem) >= 4 * WAVE_ELTS * sizeof(T), "staging space in the tile buffers");
+    T* st = &smem[0][0] + w * WAVE_ELTS;
+    const float lt = half_sum(l_run[0]);
+    const float inv = lt > 0.f ? a.rp / lt : 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        t4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = static_cast<T>(o[0][db][4 * g + e] * inv);
+        *reinterpret_cast<t4*>(&st[lo * RSE + db * 32 + 8 * g + 4 * hi]) = r;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // 32 rows x 8 pieces of 16 bytes, 64 lanes
+      const int c = i * 64 + lane;
+      const int row = c >> 3, ch = c & 7;
+      buffer_store16(ors, (q0b[0] + row) * RB + ch * 16, *reinterpret_cast<const u32x4*>(&st[row * RSE + ch * 8]));
+    }
+    buffer_store4(lrs, hi ? 0x7FFFFFF0 : qb_[0] * 4, lt > 0.f ? (m_run[0] + log2_fast(lt)) * kLn2 : NEG_INF);
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float lt = half_sum(l_run[b]);
