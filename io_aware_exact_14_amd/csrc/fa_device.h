@@ -170,6 +170,39 @@ __device__ __forceinline__ typename Mfma<T>::frag load_frag_tr(const T* tile, in
   return __builtin_bit_cast(typename Mfma<T>::frag, xy);
 }
 
+// XOR swizzle (in 16-byte chunks) of an unpadded 16-bit LDS tile row of D
+// elements: the logical chunk lc of row r sits at physical chunk
+// lc ^ lds_swizzle<D>(r). With 64 banks of 4 bytes, it keeps both read
+// patterns free of bank conflicts: 16 consecutive rows read at one logical
+// chunk (row fragments) land on 16 distinct 16-byte bank groups, and the
+// 4 rows x 4 aligned chunks that half a wave reads with a transpose read
+// do too.
+template <int D>
+__device__ __forceinline__ int lds_swizzle(int r) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  if constexpr (D == 64)
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);  // 128-byte rows: two rows per bank sweep
+  else
+    return ((r & 3) << 2) | ((r >> 2) & 3);  // 256-byte rows
+}
+
+// load_frag_tr over a swizzled, unpadded tile (rows of D elements). Each
+// lane's 8 bytes stay inside one 16-byte chunk, so only the chunk index moves.
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma<T>::frag load_frag_tr_swz(const T* tile, int base, int col0, int lane) {
+  static_assert(sizeof(T) == 2, "16-bit only");
+  const int j = lane & 15;
+  const int row = base + 4 * (lane >> 5) + (j >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const T* p0 = tile + row * D + (((col >> 3) ^ lds_swizzle<D>(row)) << 3) + (col & 7);
+  const T* p1 = tile + (row + 8) * D + (((col >> 3) ^ lds_swizzle<D>(row + 8)) << 3) + (col & 7);
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 xy = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(typename Mfma<T>::frag, xy);
+}
+
 // Whether byte `idx` of a block mask is nonzero. `idx` must be uniform across
 // the wave: the aligned dword holding the byte is read with a scalar load
 // (constant address space), which keeps the vector-memory counter free for
@@ -194,6 +227,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
+// Direct-to-LDS buffer load: lane L reads 16 bytes at `voff` (zeros past the
+// resource's range) and writes them to LDS at lds + 16 * L; `lds` must be
+// uniform across the wave (it goes into M0). Completion is counted by the
+// vector-memory counter (wait_vmem).
+typedef __attribute__((address_space(3))) void lds_void;
+template <typename T>
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, T* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, int voff, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, voff, 0, 0);
 }
