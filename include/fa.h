@@ -35,9 +35,10 @@
  * Dropout keep bits Z_ij (the pages name dropout as a fused step but give no
  * generator; this library defines one). With fmix32 the MurmurHash3 32-bit
  * finalizer (x ^= x>>16; x *= 0x85EBCA6B; x ^= x>>13; x *= 0xC2B2AE35;
- * x ^= x>>16, all mod 2^32):
+ * x ^= x>>16, all mod 2^32) and mix32 the same steps without the first
+ * shift (x *= 0x85EBCA6B; x ^= x>>13; x *= 0xC2B2AE35; x ^= x>>16):
  *   key(b,h)  = fmix32(fmix32(fmix32(fmix32(lo32(seed) + 0x9E3779B9) ^ hi32(seed)) ^ b) ^ h)
- *   u(i,j)    = fmix32(fmix32(key(b,h) ^ i) ^ j)
+ *   u(i,j)    = mix32(fmix32(key(b,h) ^ i) + j)      (sum mod 2^32)
  *   Z_ij      = u(i,j) >= T,  T = floor(dropout_p * 2^32) computed in double
  * With dropout_p == 0 no bit is drawn and Z == 1.
  */

@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   uint32_t rowhash = 0;
   if constexpr (DROP) {
     const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
-    rowhash = fmix32(hk ^ (uint32_t)q) ^ (uint32_t)(4 * hi);  // crow's 4*hi folded in (fmix32_head)
+    rowhash = fmix32(hk ^ (uint32_t)q) + (uint32_t)(4 * hi);  // crow's 4*hi folded in
   }
 
   const int kend = a.causal ? min(N, qtile0 + BR) : N;
@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
           for (int v = 0; v < 16; ++v)
             if (kb * 32 + 8 * (v >> 2) + (v & 3) > t) s[kb][v] = NEG_INF;
       }
-      const uint32_t y = fmix32_head(rowhash ^ (uint32_t)k0);  // keys k0 | offset below BC
+      const uint32_t y = (rowhash + (uint32_t)k0) * kMixMul;  // keys k0 + offset: one product per tile
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -244,7 +244,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
           float ds = kNegD ? dp[kb][v] : dp[kb][v] - Dq;
           if constexpr (DROP) {  // dP * Z / (1 - p) - D
             const uint32_t off = (uint32_t)(kb * 32 + 8 * (v >> 2) + (v & 3));
-            ds = fmix32_tail(y ^ off) >= a.thresh ? fmaf(dp[kb][v], a.rp, -Dq) : -Dq;
+            ds = keep_finish(y + off * kMixMul) >= a.thresh ? fmaf(dp[kb][v], a.rp, -Dq) : -Dq;
           }
           s[kb][v] = p * ds;  // dS^T
         }
@@ -360,7 +360,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int k0w = k0wg + w * 32;
   const int key = k0w + lo;
   const bool kvalid = key < N;
-  const uint32_t keyh = fmix32_head((uint32_t)key);  // the row words in LDS carry their head step too
+  const uint32_t keyh = (uint32_t)key * kMixMul;  // the row words in LDS are row * kMixMul
 
   // Keys past the end are clamped to row N-1: their scores are masked and
   // their gradients never stored.
@@ -421,7 +421,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const float l = Lg[qic];
     l_reg = (qi >= N || l == NEG_INF) ? POS_INF : l * kLog2e;
     d_reg = -Dg[qic];
-    if constexpr (DROP) h_reg = fmix32_head(fmix32(hk ^ (uint32_t)qi));  // head step of the (row, key) hash
+    if constexpr (DROP) h_reg = fmix32(hk ^ (uint32_t)qi) * kMixMul;  // row word times the first multiplier
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -520,7 +520,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             const float p = exp2_fast(fmaf(s[qb][v], a.sl2, -l4[e]));
             float pd = p, ds = dp[qb][v];  // dP - D
             if constexpr (DROP) {
-              const bool keep = fmix32_tail(h4[e] ^ keyh) >= a.thresh;
+              const bool keep = keep_finish(h4[e] + keyh) >= a.thresh;
               pd = keep ? p : 0.f;                                // 1 / (1 - p) goes on dV at the end
               ds = keep ? fmaf(dp[qb][v], a.rp, nd4[e]) : nd4[e];  // dP * Z / (1 - p) - D
             }

@@ -119,21 +119,21 @@ __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ float half_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float half_sum(float x) { return x + __shfl_xor(x, 32, 64); }
 
-// MurmurHash3 32-bit finalizer (Appleby, public domain), split after its
-// first step. That step is linear over XOR, fmix32_head(a ^ b) =
-// fmix32_head(a) ^ fmix32_head(b), and leaves b < 2^16 unchanged, so the keep
-// hash of a row word r and the key k0 | off (off < 2^16) is
-// fmix32_tail(fmix32_head(r ^ k0) ^ off): one word per tile, then one XOR per
-// key.
-__device__ __forceinline__ uint32_t fmix32_head(uint32_t x) { return x ^ (x >> 16); }
-__device__ __forceinline__ uint32_t fmix32_tail(uint32_t x) {
-  x *= 0x85EBCA6Bu;
+// MurmurHash3 32-bit finalizer (Appleby, public domain).
+constexpr uint32_t kMixMul = 0x85EBCA6Bu;  // its first multiplier
+__device__ __forceinline__ uint32_t keep_finish(uint32_t x) {  // the steps after that multiply
   x ^= x >> 13;
   x *= 0xC2B2AE35u;
   x ^= x >> 16;
   return x;
 }
-__device__ __forceinline__ uint32_t fmix32(uint32_t x) { return fmix32_tail(fmix32_head(x)); }
+__device__ __forceinline__ uint32_t fmix32(uint32_t x) { return keep_finish((x ^ (x >> 16)) * kMixMul); }
+
+// Keep word of row word r and key j: mix32(r + j) = keep_finish((r + j) *
+// kMixMul). The multiply distributes over the sum (mod 2^32), so a kernel
+// forms (r + tile base) * kMixMul once per tile and adds the key offset times
+// kMixMul, a compile-time constant, per key; or keeps r * kMixMul per row and
+// adds its own key's j * kMixMul.
 
 // Per-(b, h) dropout key from the 64-bit seed.
 __device__ __forceinline__ uint32_t head_key(uint32_t seed_lo, uint32_t seed_hi, uint32_t b, uint32_t h) {

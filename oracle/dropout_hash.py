@@ -9,14 +9,19 @@ the same mask without storing it:
 
     fmix32(x)  : x ^= x >> 16; x *= 0x85EBCA6B; x ^= x >> 13;
                  x *= 0xC2B2AE35; x ^= x >> 16          (all mod 2^32)
+    mix32(x)   : fmix32 without its first step:
+                 x *= 0x85EBCA6B; x ^= x >> 13; x *= 0xC2B2AE35; x ^= x >> 16
     key(b, h)  = fmix32(fmix32(fmix32(fmix32(lo(seed) + 0x9E3779B9) ^ hi(seed)) ^ b) ^ h)
     row(i)     = fmix32(key ^ i)
-    u(i, j)    = fmix32(row(i) ^ j)
+    u(i, j)    = mix32(row(i) + j)                      (sum mod 2^32)
     keep(i, j) = u(i, j) >= T,   T = floor(p * 2^32) evaluated in float64
 
 ``fmix32`` is the finalizer of Austin Appleby's MurmurHash3 (public domain).
-The oracle's copy is written here with numpy uint32 arithmetic and shares
-nothing with the GPU side.
+The key index enters by addition ahead of the first multiply, so the
+product (row(i) + j) * 0x85EBCA6B splits into a per-row and a per-key term;
+the row word is already a full fmix32 output, so the first shift of fmix32
+is left out. The oracle's copy is written here with numpy uint32 arithmetic
+and shares nothing with the GPU side.
 """
 from __future__ import annotations
 
@@ -37,6 +42,17 @@ def fmix32(x):
     a = a * np.uint32(0xC2B2AE35)
     a ^= a >> np.uint32(16)
     return int(a[0]) if scalar else a
+
+
+def mix32(x):
+    """fmix32 without its first xor-shift, on numpy uint32 values (any shape)."""
+    x = np.asarray(x, dtype=np.uint32)
+    a = np.atleast_1d(x).copy()  # array arithmetic wraps mod 2^32 without warnings
+    a = a * np.uint32(0x85EBCA6B)
+    a ^= a >> np.uint32(13)
+    a = a * np.uint32(0xC2B2AE35)
+    a ^= a >> np.uint32(16)
+    return a.reshape(x.shape)
 
 
 def head_key(seed: int, b: int, h: int) -> int:
@@ -69,5 +85,5 @@ def dropout_keep(seed: int, b: int, h: int, rows, cols, p: float) -> np.ndarray:
     T = dropout_threshold(p)
     k = np.uint32(head_key(seed, b, h))
     r = fmix32((rows.astype(np.uint32) ^ k))
-    u = fmix32(r[:, None] ^ cols.astype(np.uint32)[None, :])
+    u = mix32(r[:, None] + cols.astype(np.uint32)[None, :])  # uint32 sum wraps mod 2^32
     return u >= np.uint32(T)

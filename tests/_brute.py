@@ -32,7 +32,13 @@ def keep_bit(seed: int, b: int, h: int, i: int, j: int, p: float) -> bool:
     k = _fmix(k ^ ((seed >> 32) & M32))
     k = _fmix(k ^ b)
     k = _fmix(k ^ h)
-    u = _fmix(_fmix(k ^ i) ^ j)
+    # the key index is added to the row word, then the finalizer runs from its
+    # first multiply on (its leading shift left out)
+    x = (_fmix(k ^ i) + j) & M32
+    x = (x * 0x85EBCA6B) & M32
+    x ^= x >> 13
+    x = (x * 0xC2B2AE35) & M32
+    u = x ^ (x >> 16)
     return u >= math.floor(p * 4294967296.0)
 
 

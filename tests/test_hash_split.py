@@ -1,30 +1,28 @@
 """The split of the keep hash that the HIP kernels evaluate (CPU only).
 
-The kernels do not call fmix32 on every (row word, key) pair. They apply its
-first step, x ^ (x >> 16), once per tile and then finish each key with one
-XOR and the remaining steps. These tests check that rewriting against the
-oracle's fmix32 over every offset of a tile, for tile bases at the 16-bit
-boundary and beyond.
+The keep word is mix32(row + key), and mix32 starts with a multiply, so the
+kernels distribute it over the sum: (row + key) * C1 = row * C1 + key * C1
+(mod 2^32). The forward and dQ kernels form (row + tile base) * C1 once per
+tile and add a compile-time off * C1 per key; the dK/dV kernel keeps
+row * C1 in LDS and adds key * C1 of its lane. These tests check both
+rewritings against the oracle's mix32 for tile bases at and beyond the
+16-bit boundary and for wrapping sums.
 """
 import numpy as np
 import pytest
 
-from oracle.dropout_hash import fmix32
+from oracle.dropout_hash import mix32
 
-M32 = np.uint64(0xFFFFFFFF)
-
-
-def _head(x):
-    x = np.asarray(x, dtype=np.uint64)
-    return x ^ (x >> np.uint64(16))
+M32 = 0xFFFFFFFF
+C1 = 0x85EBCA6B
 
 
-def _tail(x):
-    x = np.asarray(x, dtype=np.uint64)
-    x = (x * np.uint64(0x85EBCA6B)) & M32
-    x ^= x >> np.uint64(13)
-    x = (x * np.uint64(0xC2B2AE35)) & M32
-    x ^= x >> np.uint64(16)
+def _finish(x):
+    # the steps of mix32 after its first multiply
+    x &= M32
+    x ^= x >> 13
+    x = (x * 0xC2B2AE35) & M32
+    x ^= x >> 16
     return x
 
 
@@ -34,27 +32,33 @@ def _crow(v, hi):
 
 
 @pytest.mark.parametrize("bc", [32, 64])
-def test_tile_word_then_one_xor_per_key(bc):
+def test_tile_word_then_one_add_per_key(bc):
     rng = np.random.default_rng(11)
-    rows = rng.integers(0, 2**32, 64, dtype=np.uint64)
-    bases = np.array([0, bc, 65536 - bc, 65536, 3 * 65536 + 7 * bc, 2**31 - bc], dtype=np.uint64)
+    rows = [int(x) for x in rng.integers(0, 2**32, 48, dtype=np.uint64)] + [M32, M32 - 5]
+    bases = [0, bc, 65536 - bc, 65536, 3 * 65536 + 7 * bc, 2**31 - bc]
     for r in rows:
         for hi in (0, 1):
-            rw = np.uint64(int(r) ^ (4 * hi))  # the lane half folded into the row word
+            rw = (r + 4 * hi) & M32  # the lane half's key offset folded into the row word
             for k0 in bases:
-                y = _head(rw ^ k0)
+                y = ((rw + k0) * C1) & M32  # once per tile
                 for kb in range(bc // 32):
                     for v in range(16):
-                        key = int(k0) + kb * 32 + _crow(v, hi)
+                        key = k0 + kb * 32 + _crow(v, hi)
                         off = kb * 32 + 8 * (v >> 2) + (v & 3)
-                        assert int(_tail(y ^ np.uint64(off))) == int(fmix32(int(r) ^ key))
+                        got = _finish(y + ((off * C1) & M32))
+                        assert got == int(mix32(np.uint32((r + key) & M32)))
 
 
-def test_row_words_with_head_step_stored():
-    # dK/dV: lanes own a key, rows come from LDS with the head step applied
+def test_row_words_times_c1_stored():
+    # dK/dV: lanes own a key; the rows' words come from LDS already times C1
     rng = np.random.default_rng(12)
-    rows = rng.integers(0, 2**32, 200, dtype=np.uint64)
+    rows = np.concatenate([rng.integers(0, 2**32, 200, dtype=np.uint64), [M32]]).astype(np.uint64)
     keys = np.concatenate([np.arange(0, 300), rng.integers(0, 2**31, 300)]).astype(np.uint64)
-    got = _tail(_head(rows)[:, None] ^ _head(keys)[None, :])
-    want = np.array([[fmix32(int(r) ^ int(k)) for k in keys] for r in rows], dtype=np.uint64)
-    np.testing.assert_array_equal(got, want)
+    side = (rows * np.uint64(C1)) & np.uint64(M32)
+    keyc = (keys * np.uint64(C1)) & np.uint64(M32)
+    x = (side[:, None] + keyc[None, :]) & np.uint64(M32)
+    x ^= x >> np.uint64(13)
+    x = (x * np.uint64(0xC2B2AE35)) & np.uint64(M32)
+    x ^= x >> np.uint64(16)
+    want = mix32((rows[:, None] + keys[None, :]).astype(np.uint32))
+    np.testing.assert_array_equal(x.astype(np.uint32), want)

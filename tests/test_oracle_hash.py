@@ -77,8 +77,12 @@ def _scalar_keep(seed, b, h, i, j, p):
     k = fmix32((lo + 0x9E3779B9) & M32)
     for word in (hi, b, h):
         k = fmix32(k ^ word)
-    u = fmix32(fmix32(k ^ i) ^ j)
-    return u >= math.floor(p * 2.0**32)
+    x = (fmix32(k ^ i) + j) & M32
+    x = (x * 0x85EBCA6B) & M32
+    x ^= x >> 13
+    x = (x * 0xC2B2AE35) & M32
+    x ^= x >> 16
+    return x >= math.floor(p * 2.0**32)
 
 
 def test_keep_bits_follow_the_stated_chain():
@@ -116,6 +120,18 @@ def test_keep_fraction_and_row_independence():
     agree = (z == z2).mean()
     ex = p * p + (1 - p) ** 2
     assert abs(agree - ex) < 6 * math.sqrt(ex * (1 - ex) / n)
+
+
+def test_neighbouring_keys_and_rows_are_uncorrelated():
+    # the key index enters by addition, so check that adjacent keys of a row,
+    # adjacent rows at one key, and the anti-diagonal neighbour agree only at
+    # the rate of independent bits, p^2 + (1-p)^2
+    for p in (0.1, 0.5):
+        z = dropout_keep(0x5EED0003, 0, 7, np.arange(1025), np.arange(1025), p)
+        ex = p * p + (1 - p) ** 2
+        for a, b in ((z[:, 1:], z[:, :-1]), (z[1:, :], z[:-1, :]), (z[1:, :-1], z[:-1, 1:])):
+            agree = (a == b).mean()
+            assert abs(agree - ex) < 6 * math.sqrt(ex * (1 - ex) / a.size), (p, agree, ex)
 
 
 def test_large_indices_wrap_as_uint32():
