@@ -36,11 +36,18 @@
  * generator; this library defines one). With fmix32 the MurmurHash3 32-bit
  * finalizer (x ^= x>>16; x *= 0x85EBCA6B; x ^= x>>13; x *= 0xC2B2AE35;
  * x ^= x>>16, all mod 2^32) and mix32 the same steps without the first
- * shift (x *= 0x85EBCA6B; x ^= x>>13; x *= 0xC2B2AE35; x ^= x>>16):
+ * shift (x *= 0x85EBCA6B; x ^= x>>13; x *= 0xC2B2AE35; x ^= x>>16), one
+ * 32-bit word serves the two keys 2m and 2m+1 of a query row:
  *   key(b,h)  = fmix32(fmix32(fmix32(fmix32(lo32(seed) + 0x9E3779B9) ^ hi32(seed)) ^ b) ^ h)
- *   u(i,j)    = mix32(fmix32(key(b,h) ^ i) + j)      (sum mod 2^32)
- *   Z_ij      = u(i,j) >= T,  T = floor(dropout_p * 2^32) computed in double
- * With dropout_p == 0 no bit is drawn and Z == 1.
+ *   w(i,m)    = mix32(fmix32(key(b,h) ^ i) + m)      (sum mod 2^32)
+ *   half(i,j) = bits [16*(j%2), 16*(j%2)+16) of w(i, j/2)  (even j: low half)
+ *   Z_ij      = half(i,j) >= T16,  T16 = floor(dropout_p * 2^16) computed in double
+ * With dropout_p == 0 no bit is drawn and Z == 1. A key is kept with
+ * probability 1 - T16/2^16 (within 2^-16 of 1 - dropout_p); kept values are
+ * scaled by 1 / (1 - dropout_p). w depends on i only through
+ * fmix32(key ^ i) + m, so two rows of a head whose row words differ by
+ * delta (|delta| < N/2) get keep masks that are copies shifted by 2*delta
+ * keys: about N^3 / 2^33 such row pairs per head.
  */
 #ifndef FA_H
 #define FA_H
@@ -52,7 +59,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 /* Element types of Q, K, V, O, dO (in_dtype) and of dQ, dK, dV (grad_dtype). */
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;

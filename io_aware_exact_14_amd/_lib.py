@@ -8,7 +8,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS_NAMES = {
     0: "FA_OK",

@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   uint32_t rowhash = 0;
   if constexpr (DROP) {
     const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
-    rowhash = fmix32(hk ^ (uint32_t)q) + (uint32_t)(4 * hi);  // crow's 4*hi folded in
+    rowhash = fmix32(hk ^ (uint32_t)q) + (uint32_t)(2 * hi);  // crow's 4*hi keys = 2*hi pairs
   }
 
   const int kend = a.causal ? min(N, qtile0 + BR) : N;
@@ -235,16 +235,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
           for (int v = 0; v < 16; ++v)
             if (kb * 32 + 8 * (v >> 2) + (v & 3) > t) s[kb][v] = NEG_INF;
       }
-      const uint32_t y = (rowhash + (uint32_t)k0) * kMixMul;  // keys k0 + offset: one product per tile
+      const uint32_t y = (rowhash + (uint32_t)(k0 >> 1)) * kMixMul;  // pairs k0/2 + offset: one product per tile
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = exp2_fast(fmaf(s[kb][v], a.sl2, -lse2));
           float ds = kNegD ? dp[kb][v] : dp[kb][v] - Dq;
-          if constexpr (DROP) {  // dP * Z / (1 - p) - D
-            const uint32_t off = (uint32_t)(kb * 32 + 8 * (v >> 2) + (v & 3));
-            ds = keep_finish(y + off * kMixMul) >= a.thresh ? fmaf(dp[kb][v], a.rp, -Dq) : -Dq;
+          if constexpr (DROP) {  // dP * Z / (1 - p) - D; elements v, v + 1 (v even) share a keep word
+            const uint32_t off = (uint32_t)(kb * 16 + 4 * (v >> 2) + ((v & 3) >> 1));
+            const uint32_t u = keep_finish(y + off * kMixMul);
+            const bool keep = (v & 1) ? keep_hi(u, a.thresh) : keep_lo(u, a.thresh);
+            ds = keep ? fmaf(dp[kb][v], a.rp, -Dq) : -Dq;
           }
           s[kb][v] = p * ds;  // dS^T
         }
@@ -360,7 +362,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int k0w = k0wg + w * 32;
   const int key = k0w + lo;
   const bool kvalid = key < N;
-  const uint32_t keyh = (uint32_t)key * kMixMul;  // the row words in LDS are row * kMixMul
+  // Dropout: keys 2m and 2m + 1 (lanes lo and lo ^ 1 of a quad) share the
+  // keep word of pair m. Each lane of the pair computes the words of half of
+  // its 16 queries per block (the even lane elements 0..7, the odd lane
+  // 8..15) and takes the other half from its neighbour by a DPP swap; the
+  // even key reads the low 16 bits, the odd key the high 16.
+  const uint32_t keyh = (uint32_t)(key >> 1) * kMixMul;  // the row words in LDS are row * kMixMul
+  const bool odd = (lo & 1) != 0;
+  const uint32_t hmask = odd ? 0xFFFF0000u : 0x0000FFFFu;
+  const uint32_t hthr = odd ? a.thresh : (a.thresh >> 16);
 
   // Keys past the end are clamped to row N-1: their scores are masked and
   // their gradients never stored.
@@ -503,24 +513,39 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             if (qb * 32 + 8 * (v >> 2) + (v & 3) < t) s[qb][v] = NEG_INF;
       }
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+      for (int qb = 0; qb < NQB; ++qb) {
+        bool kbit[16];  // keep bit of element v (dropout only)
+        if constexpr (DROP) {
+          uint32_t wown[8];  // words of elements 8 * odd + e
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            const u32x4 h4 = *reinterpret_cast<const u32x4*>(&side_h[cur][qb * 32 + 8 * (gg + 2 * (int)odd) + 4 * hi]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wown[4 * gg + e] = keep_finish(h4[e] + keyh);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            // quad_perm [1, 0, 3, 2]: the neighbour's word, elements 8 * (1 - odd) + e
+            const uint32_t wnb = (uint32_t)__builtin_amdgcn_mov_dpp((int)wown[e], 0xB1, 0xF, 0xF, true);
+            const uint32_t wlo = odd ? wnb : wown[e];  // word of element e
+            const uint32_t whi = odd ? wown[e] : wnb;  // word of element e + 8
+            kbit[e] = (wlo & hmask) >= hthr;
+            kbit[e + 8] = (whi & hmask) >= hthr;
+          }
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ql = qb * 32 + 8 * g + 4 * hi;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&side_l[cur][ql]);
           f32x4 nd4 = {0.f, 0.f, 0.f, 0.f};  // -D
-          u32x4 h4 = {0, 0, 0, 0};
-          if constexpr (DROP) {
-            nd4 = *reinterpret_cast<const f32x4*>(&side_d[cur][ql]);
-            h4 = *reinterpret_cast<const u32x4*>(&side_h[cur][ql]);
-          }
+          if constexpr (DROP) nd4 = *reinterpret_cast<const f32x4*>(&side_d[cur][ql]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * g + e;
             const float p = exp2_fast(fmaf(s[qb][v], a.sl2, -l4[e]));
             float pd = p, ds = dp[qb][v];  // dP - D
             if constexpr (DROP) {
-              const bool keep = keep_finish(h4[e] + keyh) >= a.thresh;
+              const bool keep = kbit[v];
               pd = keep ? p : 0.f;                                // 1 / (1 - p) goes on dV at the end
               ds = keep ? fmaf(dp[qb][v], a.rp, nd4[e]) : nd4[e];  // dP * Z / (1 - p) - D
             }
@@ -528,6 +553,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             dp[qb][v] = p * ds;  // dS
           }
         }
+      }
       if constexpr (KH == 8) {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)

@@ -129,11 +129,17 @@ __device__ __forceinline__ uint32_t keep_finish(uint32_t x) {  // the steps afte
 }
 __device__ __forceinline__ uint32_t fmix32(uint32_t x) { return keep_finish((x ^ (x >> 16)) * kMixMul); }
 
-// Keep word of row word r and key j: mix32(r + j) = keep_finish((r + j) *
-// kMixMul). The multiply distributes over the sum (mod 2^32), so a kernel
-// forms (r + tile base) * kMixMul once per tile and adds the key offset times
-// kMixMul, a compile-time constant, per key; or keeps r * kMixMul per row and
-// adds its own key's j * kMixMul.
+// Keep word of row word r and key pair m = j / 2: mix32(r + m) =
+// keep_finish((r + m) * kMixMul); key 2m reads its low 16 bits, key 2m + 1
+// its high 16 bits. The multiply distributes over the sum (mod 2^32), so a
+// kernel forms (r + tile's first pair) * kMixMul once per tile and adds the
+// pair offset times kMixMul, a compile-time constant, per pair; or keeps
+// r * kMixMul per row and adds its own pair's m * kMixMul.
+//
+// With thresh = T16 << 16 (T16 = floor(p * 2^16)): the high half is kept iff
+// u >= thresh, the low half iff (u << 16) >= thresh.
+__device__ __forceinline__ bool keep_hi(uint32_t u, uint32_t thresh) { return u >= thresh; }
+__device__ __forceinline__ bool keep_lo(uint32_t u, uint32_t thresh) { return (u << 16) >= thresh; }
 
 // Per-(b, h) dropout key from the 64-bit seed.
 __device__ __forceinline__ uint32_t head_key(uint32_t seed_lo, uint32_t seed_hi, uint32_t b, uint32_t h) {

@@ -12,7 +12,9 @@ __global__ void __launch_bounds__(256) dropout_mask_kernel(uint32_t hk, uint32_t
   if (idx >= rows * cols) return;
   const int64_t r = idx / cols, c = idx - r * cols;
   const uint32_t rh = fmix32(hk ^ (uint32_t)(i0 + r));
-  keep[idx] = keep_finish((rh + (uint32_t)(j0 + c)) * kMixMul) >= thresh ? 1 : 0;
+  const uint32_t j = (uint32_t)(j0 + c);
+  const uint32_t u = keep_finish((rh + (j >> 1)) * kMixMul);
+  keep[idx] = ((j & 1u) ? keep_hi(u, thresh) : keep_lo(u, thresh)) ? 1 : 0;
 }
 
 // Host-side copy of the per-(b, h) key derivation (same steps as head_key).

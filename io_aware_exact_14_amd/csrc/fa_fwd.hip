@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   if constexpr (DROP) {
     const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
 #pragma unroll
-    for (int b = 0; b < QB; ++b) rowhash[b] = fmix32(hk ^ (uint32_t)qb_[b]) + (uint32_t)(4 * hi);  // crow's 4*hi folded in
+    for (int b = 0; b < QB; ++b) rowhash[b] = fmix32(hk ^ (uint32_t)qb_[b]) + (uint32_t)(2 * hi);  // crow's 4*hi keys = 2*hi pairs
   }
 
   // KV tiles this workgroup visits: causal stops at its diagonal; a block
@@ -289,15 +289,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         l_run[b] += rs;
 
         if constexpr (DROP) {
-          // Keys k0 + kb*32 + crow(v, hi): one product per tile, then a
-          // constant per key (keep_finish).
-          const uint32_t y = (rowhash[b] + (uint32_t)k0) * kMixMul;
+          // Keys k0 + kb*32 + crow(v, hi); elements v and v + 1 (v even) are
+          // the two keys of pair k0/2 + kb*16 + 4*(v/4) + 2*hi + (v%4)/2: one
+          // product per tile, then a constant per pair (keep_finish) whose
+          // low half decides the even key and high half the odd one.
+          const uint32_t y = (rowhash[b] + (uint32_t)(k0 >> 1)) * kMixMul;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const uint32_t off = (uint32_t)(kb * 32 + 8 * (v >> 2) + (v & 3));
-              s[b][kb][v] = keep_finish(y + off * kMixMul) < a.thresh ? 0.f : s[b][kb][v];
+            for (int v = 0; v < 16; v += 2) {
+              const uint32_t off = (uint32_t)(kb * 16 + 4 * (v >> 2) + ((v & 3) >> 1));
+              const uint32_t u = keep_finish(y + off * kMixMul);
+              s[b][kb][v] = keep_lo(u, a.thresh) ? s[b][kb][v] : 0.f;
+              s[b][kb][v + 1] = keep_hi(u, a.thresh) ? s[b][kb][v + 1] : 0.f;
             }
         }
       }

@@ -20,12 +20,16 @@ Parity status of each function (see the pins in ``tests/test_oracle_*.py``):
 * ``backward_rows`` (dQ of selected rows) and ``backward_cols`` (dK, dV of
   selected keys): pinned by central finite differences with respect to those
   rows of Q, K and V.
-* ``dropout_keep``: pinned for the mixing function by the published
-  MurmurHash3 test vectors; the chaining of (seed, b, h, i, j) is this
-  library's own definition ("parity unpinned" beyond that definition and the
+* ``fmix32``: pinned by the published MurmurHash3_x86_32 test vectors.
+* ``mix32``: pinned to fmix32 by the identity mix32(x ^ (x >> 16)) == fmix32(x).
+* ``head_key`` / ``row_words``: fmix32 chains, pinned against fmix32 composed
+  step by step.
+* ``dropout_keep`` / ``keep_halves``: the way (seed, b, h, i, j) are chained
+  and split into 16-bit halves is this library's own definition ("parity
+  unpinned" beyond that definition, the bijection it implies and the
   statistical checks).
 """
-from .dropout_hash import fmix32, head_key, dropout_threshold, dropout_keep  # noqa: F401
+from .dropout_hash import fmix32, mix32, head_key, row_words, dropout_threshold, keep_halves, dropout_keep  # noqa: F401
 from .attention import (  # noqa: F401
     valid_mask,
     forward_head,

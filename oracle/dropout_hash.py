@@ -5,7 +5,8 @@ the fused step list (FlashAttention milestone page, section "The idea", the
 paragraph on the single kernel; inferensys glossary, "Kernel Fusion") but do
 not say how the random bits are drawn. This library defines them as a
 counter-based hash of (seed, b, h, i, j), so forward and backward regenerate
-the same mask without storing it:
+the same mask without storing it. One 32-bit word serves two neighbouring
+keys: key 2m reads its low 16 bits and key 2m+1 its high 16 bits.
 
     fmix32(x)  : x ^= x >> 16; x *= 0x85EBCA6B; x ^= x >> 13;
                  x *= 0xC2B2AE35; x ^= x >> 16          (all mod 2^32)
@@ -13,15 +14,26 @@ the same mask without storing it:
                  x *= 0x85EBCA6B; x ^= x >> 13; x *= 0xC2B2AE35; x ^= x >> 16
     key(b, h)  = fmix32(fmix32(fmix32(fmix32(lo(seed) + 0x9E3779B9) ^ hi(seed)) ^ b) ^ h)
     row(i)     = fmix32(key ^ i)
-    u(i, j)    = mix32(row(i) + j)                      (sum mod 2^32)
-    keep(i, j) = u(i, j) >= T,   T = floor(p * 2^32) evaluated in float64
+    w(i, m)    = mix32(row(i) + m)                      (sum mod 2^32)
+    half(i, j) = (w(i, floor(j / 2)) >> (16 * (j mod 2))) mod 2^16
+    keep(i, j) = half(i, j) >= T16,   T16 = floor(p * 2^16) evaluated in float64
 
-``fmix32`` is the finalizer of Austin Appleby's MurmurHash3 (public domain).
-The key index enters by addition ahead of the first multiply, so the
-product (row(i) + j) * 0x85EBCA6B splits into a per-row and a per-key term;
-the row word is already a full fmix32 output, so the first shift of fmix32
-is left out. The oracle's copy is written here with numpy uint32 arithmetic
-and shares nothing with the GPU side.
+``fmix32`` is the finalizer of Austin Appleby's MurmurHash3 (public domain);
+``mix32(x ^ (x >> 16)) == fmix32(x)`` ties the two. The pair index enters by
+addition ahead of the first multiply, so the product
+(row(i) + m) * 0x85EBCA6B splits into a per-row and a per-pair term; the row
+word is already a full fmix32 output, so the first shift of fmix32 is left
+out. A kept element has probability 1 - T16 / 2^16, which lies within 2^-16
+of 1 - p; the surviving values are scaled by 1 / (1 - p) all the same.
+
+Because w depends on i only through row(i) + m, two rows whose row words
+differ by a small delta (|delta| < N/2) draw the same words shifted by delta
+pairs: their keep masks agree after a shift of 2 * delta keys. Over the
+N^2/2 row pairs of a head about N^3 / 2^33 are such pairs (1 at N = 2048,
+about 500 at N = 16384).
+
+The oracle's copy is written here with numpy uint32 arithmetic and shares
+nothing with the GPU side.
 """
 from __future__ import annotations
 
@@ -66,11 +78,27 @@ def head_key(seed: int, b: int, h: int) -> int:
     return k
 
 
+def row_words(seed: int, b: int, h: int, rows) -> np.ndarray:
+    """row(i) = fmix32(key(b, h) ^ i) for the given query rows (uint32)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return fmix32(rows.astype(np.uint32) ^ np.uint32(head_key(seed, b, h)))
+
+
 def dropout_threshold(p: float) -> int:
-    """Integer threshold T = floor(p * 2^32) in float64; keep iff hash >= T."""
+    """Threshold T16 = floor(p * 2^16) in float64; keep iff the 16-bit half >= T16."""
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must lie in [0, 1)")
-    return int(math.floor(float(p) * 4294967296.0))
+    return int(math.floor(float(p) * 65536.0))
+
+
+def keep_halves(seed: int, b: int, h: int, rows, cols) -> np.ndarray:
+    """The 16-bit value half(i, j) that decides key j of query row i (uint32
+    array ``[len(rows)][len(cols)]``, values below 2^16)."""
+    cols = np.asarray(cols, dtype=np.int64)
+    r = row_words(seed, b, h, rows)
+    w = mix32(r[:, None] + (cols // 2).astype(np.uint32)[None, :])  # uint32 sum wraps mod 2^32
+    shift = (np.uint32(16) * (cols % 2).astype(np.uint32))[None, :]
+    return (w >> shift) & np.uint32(0xFFFF)
 
 
 def dropout_keep(seed: int, b: int, h: int, rows, cols, p: float) -> np.ndarray:
@@ -82,8 +110,4 @@ def dropout_keep(seed: int, b: int, h: int, rows, cols, p: float) -> np.ndarray:
     cols = np.asarray(cols, dtype=np.int64)
     if p == 0.0:
         return np.ones((rows.size, cols.size), dtype=bool)
-    T = dropout_threshold(p)
-    k = np.uint32(head_key(seed, b, h))
-    r = fmix32((rows.astype(np.uint32) ^ k))
-    u = mix32(r[:, None] + cols.astype(np.uint32)[None, :])  # uint32 sum wraps mod 2^32
-    return u >= np.uint32(T)
+    return keep_halves(seed, b, h, rows, cols) >= np.uint32(dropout_threshold(p))

@@ -32,14 +32,16 @@ def keep_bit(seed: int, b: int, h: int, i: int, j: int, p: float) -> bool:
     k = _fmix(k ^ ((seed >> 32) & M32))
     k = _fmix(k ^ b)
     k = _fmix(k ^ h)
-    # the key index is added to the row word, then the finalizer runs from its
-    # first multiply on (its leading shift left out)
-    x = (_fmix(k ^ i) + j) & M32
+    # keys 2m and 2m+1 share one word: the pair index is added to the row
+    # word, the finalizer runs from its first multiply on (its leading shift
+    # left out), and the key takes the low (even j) or high (odd j) 16 bits
+    x = (_fmix(k ^ i) + j // 2) & M32
     x = (x * 0x85EBCA6B) & M32
     x ^= x >> 13
     x = (x * 0xC2B2AE35) & M32
     u = x ^ (x >> 16)
-    return u >= math.floor(p * 4294967296.0)
+    half = (u >> 16) if j % 2 else (u & 0xFFFF)
+    return half >= math.floor(p * 65536.0)
 
 
 def is_valid(i: int, j: int, causal: bool, block_mask, mask_block: int) -> bool:

@@ -63,9 +63,9 @@ def test_header_declarations_are_exported(lib, L):
 
 
 def test_abi_version_and_struct_layout(lib, L):
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
     header = open(os.path.join(ROOT, "include", "fa.h")).read()
-    assert "#define FA_ABI_VERSION 1" in header
+    assert "#define FA_ABI_VERSION 2" in header
     # natural C layout of fa_params on x86-64
     assert ctypes.sizeof(L.FaParams) == 80
     assert L.FaParams.dropout_p.offset == 48 and L.FaParams.block_mask.offset == 64

@@ -65,3 +65,70 @@ def test_keep_bits_used_inside_forward(fa, p, dtype):
                 np.testing.assert_array_equal(np.rint(got).astype(bool), Z)
                 assert np.abs(got - np.rint(got)).max() < 0.02
             np.testing.assert_allclose(lse.cpu().numpy()[b, h], math.log(128), atol=1e-5)
+
+
+@pytest.mark.parametrize("N", [1024, 4096, 4608])
+@pytest.mark.parametrize("p", [0.1, 0.37])
+def test_keep_bits_inside_d64_kernels(fa, N, p):
+    # The d = 64 launch configurations (the dropout workload's: forward with
+    # 64-key tiles, dQ with 32-key tiles up to 4096 keys and 64-key tiles
+    # beyond, dK/dV with 32-row tiles up to 2048 keys and 64-row tiles beyond)
+    # decode every keep bit they use. Q = 0 and a permutation block mask make
+    # P = 1/128 over one kept 128-key block per query block. Two-level one-hot
+    # rows carry two bits per column: X_j = e_{j mod 64} * (1 if j mod 128 < 64
+    # else 2), so a column of the product reads Z_1 + 2 Z_2 for the two keys
+    # (or queries) that share it.
+    #   forward, V = X:       O_i[c]  = (Z_{i,j0+c} + 2 Z_{i,j0+64+c}) / (128 (1 - p))
+    #   dK/dV,   dO = X:      dV_j[c] = (Z_{i0+c,j} + 2 Z_{i0+64+c,j}) / (128 (1 - p))
+    #   dQ, K = X, V = 1, dO = e_0:  D_i = O_i[0] and
+    #                         dQ_i[c] = scale/128 * ((Z_{i,j0+c} + 2 Z_{i,j0+64+c}) / (1 - p) - 3 D_i)
+    d, mb = 64, 128
+    nb = N // mb
+    perm = np.random.default_rng(N).permutation(nb)
+    bm = np.zeros((nb, nb), np.uint8)
+    bm[np.arange(nb), perm] = 1
+    B, H, seed, dtype = 1, 2, 0xA5A5F00D0123, torch.bfloat16
+    scale = 1.0 / math.sqrt(d)
+    ar = torch.arange(N)
+    lvl = torch.where(ar % 128 < 64, 1.0, 2.0)
+    X = torch.zeros(B, H, N, d)
+    X[:, :, ar, ar % 64] = lvl
+    X = X.to(dtype)
+    q = torch.zeros(B, H, N, d, dtype=dtype)
+    e0 = torch.zeros(B, H, N, d, dtype=dtype)
+    e0[:, :, :, 0] = 1
+    ones = torch.ones(B, H, N, d, dtype=dtype)
+    kw = dict(scale=scale, dropout_p=p, seed=seed, block_mask=torch.from_numpy(bm), mask_block=mb)
+    note(f"dropout probe d=64 N={N} p={p}")
+    krand = torch.randn(B, H, N, d).to(dtype)
+    # forward and dK/dV: K arbitrary (Q = 0 ignores it), V = X, dO = X
+    qd, kd, vd = to_dev(q, krand, X)
+    o1, l1 = fa.forward(qd, kd, vd, **kw)
+    _, _, dv = fa.backward(qd, kd, vd, o1, l1, X.cuda(), **kw)
+    # dQ: K = X, V = 1, dO = e_0
+    qd2, kd2, vd2 = to_dev(q, X, ones)
+    o2, l2 = fa.forward(qd2, kd2, vd2, **kw)
+    dq, _, _ = fa.backward(qd2, kd2, vd2, o2, l2, e0.cuda(), **kw)
+    torch.cuda.synchronize()
+    o1, dv, o2, dq = (t.float().cpu().numpy() for t in (o1, dv, o2, dq))
+    u = 1.0 / (128 * (1 - p))
+
+    def levels(x):
+        r = np.rint(x)
+        assert np.abs(x - r).max() < 0.1, np.abs(x - r).max()
+        assert r.min() >= 0 and r.max() <= 3
+        return r.astype(np.int64)
+
+    for b in range(B):
+        for h in range(H):
+            for r in range(nb):
+                rows = np.arange(r * mb, (r + 1) * mb)
+                keys = np.arange(perm[r] * mb, (perm[r] + 1) * mb)
+                Z = oracle.dropout_keep(seed, b, h, rows, keys, p).astype(np.int64)
+                want_rows = Z[:, :64] + 2 * Z[:, 64:]      # [query][c]
+                want_keys = Z[:64, :].T + 2 * Z[64:, :].T  # [key][c]
+                np.testing.assert_array_equal(levels(o1[b, h][rows] / u), want_rows)
+                np.testing.assert_array_equal(levels(dv[b, h][keys] / u), want_keys)
+                D = o2[b, h][rows][:, :1]
+                g = dq[b, h][rows] * 128 / scale
+                np.testing.assert_array_equal(levels((g + 3 * D) * (1 - p)), want_rows)
