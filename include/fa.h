@@ -24,9 +24,12 @@
  * a call returns and holds no mutable global state (calls are thread-safe).
  *
  * Errors: every entry point validates its arguments on the host first; on a
- * failed check it returns a nonzero fa_status and enqueues nothing. A launch
- * failure returns FA_ERR_HIP. Faults inside kernels surface at the caller's
- * next synchronization. No C++ exception crosses this ABI.
+ * failed check it returns a nonzero fa_status and enqueues nothing. Before
+ * launching it clears the calling thread's pending HIP error (left by
+ * earlier work, not by this call), so FA_ERR_HIP reports a failure of this
+ * call's own launches. Faults inside kernels surface at the caller's next
+ * synchronization. No C++ exception crosses this ABI. Launches go to the
+ * current HIP device, which must be the device of `stream`.
  *
  * Conventions: a query row with no valid key yields O_i = 0, LSE_i = -inf
  * and zero gradient contributions. NaN/Inf inputs propagate without any
@@ -103,8 +106,12 @@ const char* fa_status_string(int status);
 int fa_check_params(const fa_params* p);
 
 /*
- * Forward pass. Reads Q, K, V; writes O (in_dtype) and LSE (fp32, natural
- * log). Enqueued asynchronously on `stream` (a hipStream_t; NULL = default).
+ * Forward pass (FlashAttention milestone page, "The idea": score product,
+ * mask, softmax, dropout and value product fused, the softmax computed
+ * tile by tile from a running row maximum and sum). Reads Q, K, V; writes O
+ * (in_dtype) and LSE (fp32, natural log; the pages keep two numbers per row,
+ * LSE_i = m_i + log l_i carries both). Enqueued asynchronously on `stream`
+ * (a hipStream_t; NULL = default).
  */
 int fa_fwd(const fa_params* p, const void* Q, const void* K, const void* V,
            void* O, float* LSE, void* stream);
@@ -113,10 +120,13 @@ int fa_fwd(const fa_params* p, const void* Q, const void* K, const void* V,
 size_t fa_bwd_workspace_bytes(const fa_params* p);
 
 /*
- * Backward pass (recomputes S and P from Q, K and LSE). Reads Q, K, V, O,
- * LSE, dO; writes dQ, dK, dV (grad_dtype). `workspace` is caller-owned
- * device memory of at least fa_bwd_workspace_bytes(p) bytes; its contents on
- * entry do not matter and on return are unspecified.
+ * Backward pass (FlashAttention milestone page, "The idea": the backward
+ * recomputes S and P tile by tile from Q, K and the stored row statistics
+ * instead of reading an N x N matrix; pixelation article, "The Recomputation
+ * Trade-off"). Reads Q, K, V, O, LSE, dO; writes dQ, dK, dV (grad_dtype).
+ * `workspace` is caller-owned device memory of at least
+ * fa_bwd_workspace_bytes(p) bytes; its contents on entry do not matter and
+ * on return are unspecified.
  */
 int fa_bwd(const fa_params* p, const void* Q, const void* K, const void* V,
            const void* O, const float* LSE, const void* dO,
@@ -139,7 +149,9 @@ int fa_bwd_dkdv(const fa_params* p, const void* Q, const void* K, const void* V,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Writes the dropout keep bits Z_ij (1 = kept) of head (b, h) for query rows
+ * Dropout keep bits (FlashAttention milestone page, "The idea": dropout is
+ * one of the fused steps, regenerated in the backward rather than stored).
+ * Writes the keep bits Z_ij (1 = kept) of head (b, h) for query rows
  * [i0, i0+rows) and key columns [j0, j0+cols) into the DEVICE buffer
  * keep[rows][cols], with the same device function the fused kernels use.
  * Masking (causal, block mask) is not applied. With dropout_p == 0 every bit

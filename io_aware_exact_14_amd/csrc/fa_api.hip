@@ -1,6 +1,7 @@
 // C-ABI host layer of libfa: argument validation, kernel selection and
 // launch on the caller's stream. Declarations and the contract of every
 // entry point are in include/fa.h.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -11,6 +12,45 @@
 namespace {
 
 constexpr int64_t kMaxI32 = 2147483647;
+constexpr int kMaxDevices = 64;
+
+// Compute units and XCDs of each device, read once (the tile orders and the
+// resident-grid test of the kernels follow the device's topology).
+std::atomic<int> g_ncu[kMaxDevices];
+std::atomic<int> g_nxcd[kMaxDevices];
+
+hipError_t device_topology(int& ncu, int& nxcd) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && g_ncu[dev].load(std::memory_order_acquire) > 0) {
+    ncu = g_ncu[dev].load(std::memory_order_acquire);
+    nxcd = g_nxcd[dev].load(std::memory_order_acquire);
+    return hipSuccess;
+  }
+  int c = 0, x = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || x <= 0) {
+    (void)hipGetLastError();  // attribute not reported: treat the device as one die
+    x = 1;
+  }
+  ncu = c > 0 ? c : 1;
+  nxcd = x;
+  if (cached) {
+    g_nxcd[dev].store(nxcd, std::memory_order_release);
+    g_ncu[dev].store(ncu, std::memory_order_release);
+  }
+  return hipSuccess;
+}
+
+// Clears a pending error that earlier work of the calling thread left behind
+// (it is not this call's), then fills in the device topology.
+hipError_t prepare_launch(fa::AttnArgs& a) {
+  (void)hipGetLastError();
+  return device_topology(a.ncu, a.nxcd);
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -95,7 +135,8 @@ int fa_fwd(const fa_params* p, const void* Q, const void* K, const void* V, void
   // Any p > 0 takes the dropout kernels, even when floor(p * 2^32) is 0 and
   // every element is kept: the output is still scaled by 1 / (1 - p).
   const bool dropout = p->dropout_p > 0.0;
-  const hipError_t e = fa::launch_fwd(elt(p->in_dtype), (int)p->d, dropout, a, (hipStream_t)stream);
+  hipError_t e = prepare_launch(a);
+  if (e == hipSuccess) e = fa::launch_fwd(elt(p->in_dtype), (int)p->d, dropout, a, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -135,8 +176,10 @@ int bwd_stage(int stage, const fa_params* p, const void* Q, const void* K, const
   a.dk = dK;
   a.dv = dV;
   a.delta = static_cast<float*>(workspace);
-  const hipError_t e = fa::launch_bwd(elt(p->in_dtype), elt(p->grad_dtype), (int)p->d, p->dropout_p > 0.0, stage,
-                                      a, (hipStream_t)stream);
+  hipError_t e = prepare_launch(a);
+  if (e == hipSuccess)
+    e = fa::launch_bwd(elt(p->in_dtype), elt(p->grad_dtype), (int)p->d, p->dropout_p > 0.0, stage, a,
+                       (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -167,8 +210,9 @@ int fa_dropout_mask(const fa_params* p, int64_t b, int64_t h, int64_t i0, int64_
   if (i0 < 0 || rows < 0 || j0 < 0 || cols < 0 || i0 + rows > p->N || j0 + cols > p->N) return FA_ERR_RANGE;
   if (rows > 0 && cols > kMaxI32 * 256 / rows) return FA_ERR_RANGE;
   if (rows * cols == 0) return FA_OK;
-  const fa::AttnArgs a = make_args(p);
-  const hipError_t e = fa::launch_dropout_mask(a, (int)b, (int)h, i0, rows, j0, cols, keep, (hipStream_t)stream);
+  fa::AttnArgs a = make_args(p);
+  hipError_t e = prepare_launch(a);
+  if (e == hipSuccess) e = fa::launch_dropout_mask(a, (int)b, (int)h, i0, rows, j0, cols, keep, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

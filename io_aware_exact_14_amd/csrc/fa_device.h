@@ -259,26 +259,30 @@ __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int voff
 __device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 // Workgroup id -> (rank, bh). A head's tiles are ranked by decreasing work
-// (causal: the tile of longest rows first). Ids are dealt round-robin over the
-// 8 XCDs, and each XCD hands its ids to its 32 CUs in turn. In the plain order
-// (id = rank * BH + bh) consecutive ids are different heads of one rank, so
-// with BH a multiple of 8 all tiles of a head land on one XCD (bh % 8 equals
-// id % 8) and share its L2. `balance` is for a grid that is resident all at
-// once, with work falling linearly in the rank: an XCD's ids then run over its
-// (rank, head) pairs in rounds of 32, forward in even rounds and backward in
-// odd ones, so a CU that drew a long tile in one round draws a short one in
-// the next and the CUs' totals even out (8 tiles a head, 16 heads an XCD: 18
-// tile-units on every CU, where the plain order gives half the CUs 20 and half
-// 16). Heads stay on their XCD either way. A grid that is not all resident
-// keeps the plain longest-first order, which a CU freeing a slot follows.
-__device__ __forceinline__ void tile_order(int id, int nq, int BH, bool balance, int& rank, int& bh) {
-  const int hpx = BH >> 3;  // heads per XCD
-  if (balance && (BH & 7) == 0 && ((nq * hpx) & 31) == 0) {
-    const int x = id & 7, n = id >> 3;
-    const int r = n >> 5, c = n & 31;
-    const int k = (r << 5) + ((r & 1) ? 31 - c : c);
+// (causal: the tile of longest rows first). Ids are dealt round-robin over
+// the device's nxcd XCDs, and each XCD hands its ids to its CUs in turn. In
+// the plain order (id = rank * BH + bh) consecutive ids are different heads
+// of one rank, so with BH a multiple of nxcd all tiles of a head land on one
+// XCD (bh % nxcd equals id % nxcd) and share its L2. `balance` is for a grid
+// that is resident all at once, with work falling linearly in the rank: an
+// XCD's ids then run over its (rank, head) pairs in rounds of one per CU,
+// forward in even rounds and backward in odd ones, so a CU that drew a long
+// tile in one round draws a short one in the next and the CUs' totals even
+// out (MI355X, 8 XCDs of 32 CUs, 8 tiles a head and 16 heads an XCD: 18
+// tile-units on every CU, where the plain order gives half the CUs 20 and
+// half 16). Heads stay on their XCD either way. A grid that is not all
+// resident keeps the plain longest-first order, which a CU freeing a slot
+// follows.
+__device__ __forceinline__ void tile_order(int id, int nq, int BH, bool balance, int ncu, int nxcd, int& rank,
+                                           int& bh) {
+  const int cpx = ncu / nxcd;  // CUs per XCD
+  if (balance && nxcd > 0 && cpx > 0 && BH % nxcd == 0 && (nq * (BH / nxcd)) % cpx == 0) {
+    const int hpx = BH / nxcd;  // heads per XCD
+    const int x = id % nxcd, n = id / nxcd;
+    const int r = n / cpx, c = n - r * cpx;
+    const int k = r * cpx + ((r & 1) ? cpx - 1 - c : c);
     rank = k / hpx;
-    bh = (k - rank * hpx) * 8 + x;
+    bh = (k - rank * hpx) * nxcd + x;
   } else {
     rank = id / BH;
     bh = id - rank * BH;

@@ -84,12 +84,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lo = lane & 31, hi = lane >> 5;
 
-  // Causal: longest rows first; a grid that fits the 256 CUs at WPE
+  // Causal: longest rows first; a grid that fits the device's CUs at WPE
   // workgroups each balances their loads (tile_order).
   const int N = a.N;
   const int nq = (N + C::BR - 1) / C::BR;
   int rank, bh;
-  tile_order((int)blockIdx.x, nq, a.BH, a.causal && nq * a.BH <= 256 * WPE, rank, bh);
+  tile_order((int)blockIdx.x, nq, a.BH, a.causal && nq * a.BH <= a.ncu * WPE, a.ncu, a.nxcd, rank, bh);
   const int qt = a.causal ? (nq - 1 - rank) : rank;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const T* __restrict__ Kg = static_cast<const T*>(a.k) + hoff;

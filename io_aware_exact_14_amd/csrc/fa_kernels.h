@@ -37,6 +37,8 @@ struct AttnArgs {
                      // 16-bit half of the keep word, moved to the top bits, is >= thresh
   uint32_t seed_lo;
   uint32_t seed_hi;
+  int ncu;           // compute units of the device the call runs on
+  int nxcd;          // accelerator complex dies (XCDs) among which workgroup ids are dealt
 };
 
 hipError_t launch_fwd(Elt t, int d, bool dropout, const AttnArgs& a, hipStream_t s);
