@@ -79,8 +79,13 @@ typedef enum {
   FA_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than fa_bwd_workspace_bytes */
   FA_ERR_HIP = 9,         /* the HIP runtime reported an error at launch */
   FA_ERR_SCALE = 10,      /* scale not finite and > 0 */
-  FA_ERR_RANGE = 11       /* fa_dropout_mask window, (b, h) or size out of range */
+  FA_ERR_RANGE = 11,      /* fa_dropout_mask window, (b, h) or size out of range */
+  FA_ERR_SCRATCH = 12     /* fa_bwd_noalloc: B*H*N above FA_BWD_NOALLOC_MAX_ROWS */
 } fa_status;
+
+/* Rows (B*H*N) that the fixed device scratch of fa_bwd_noalloc holds: 2^22
+ * fp32 values, 16 MiB per GPU. */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 22)
 
 typedef struct {
   int64_t B, H, N, d;       /* batch, heads, sequence length, head dimension */
@@ -141,6 +146,22 @@ int fa_bwd(const fa_params* p, const void* Q, const void* K, const void* V,
  * with the same parameters, inputs and workspace. fa_bwd == fa_bwd_dq
  * followed by fa_bwd_dkdv on one stream.
  */
+/*
+ * fa_bwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). D_i goes to a fixed
+ * device array of FA_BWD_NOALLOC_MAX_ROWS fp32 values inside the library
+ * (one per GPU, held until the process ends; its address is looked up on
+ * the first call on each device). B*H*N above that maximum returns
+ * FA_ERR_SCRATCH and enqueues nothing. All calls on one GPU share the array
+ * and nothing needs clearing between them (each call writes every D_i it
+ * reads); two calls that overlap on one GPU (other streams, other threads)
+ * race on it. Results are bit-identical to fa_bwd.
+ */
+int fa_bwd_noalloc(const fa_params* p, const void* Q, const void* K, const void* V,
+                   const void* O, const float* LSE, const void* dO,
+                   void* dQ, void* dK, void* dV, void* stream);
+
 int fa_bwd_dq(const fa_params* p, const void* Q, const void* K, const void* V,
               const void* O, const float* LSE, const void* dO, void* dQ,
               void* workspace, size_t workspace_bytes, void* stream);

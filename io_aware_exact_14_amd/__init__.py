@@ -22,8 +22,8 @@ from ._lib import FA_BF16, FA_F16, FA_F32, FaParams, STATUS_NAMES
 
 _lib.load()
 
-__all__ = ["forward", "backward", "backward_dq", "backward_dkdv", "dropout_mask", "bwd_workspace_bytes",
-           "FaError", "params"]
+__all__ = ["forward", "backward", "backward_noalloc", "backward_dq", "backward_dkdv", "dropout_mask",
+           "bwd_workspace_bytes", "FaError", "params"]
 
 _DT = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
@@ -143,6 +143,27 @@ def backward(q, k, v, o, lse, do, *, scale=None, causal=False, dropout_p=0.0, se
     _check(lib.fa_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *_ws(workspace), _stream()),
            "fa_bwd")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, lse, do, *, dq, dk, dv, scale=None, causal=False, dropout_p=0.0, seed=0,
+                     block_mask=None, mask_block=128, grad_dtype=torch.float32):
+    """dQ, dK, dV through fa_bwd_noalloc: no workspace and no allocation (the
+    library keeps D in a fixed per-GPU array; B*H*N up to
+    _lib.BWD_NOALLOC_MAX_ROWS). The gradients are caller-provided; a block
+    mask should already be a contiguous uint8 device tensor."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _require(t, name, (B, H, N, d), q.dtype)
+    _require(lse, "lse", (B, H, N), torch.float32)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _require(t, name, (B, H, N, d), grad_dtype)
+    bm = _mask_arg(block_mask, N, mask_block, q.device)
+    p = params(B, H, N, d, q.dtype, grad_dtype=grad_dtype, scale=scale, causal=causal, dropout_p=dropout_p,
+               seed=seed, block_mask=bm, mask_block=mask_block)
+    _check(_lib.load().fa_bwd_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                      _stream()), "fa_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -23,7 +23,9 @@ STATUS_NAMES = {
     9: "FA_ERR_HIP",
     10: "FA_ERR_SCALE",
     11: "FA_ERR_RANGE",
+    12: "FA_ERR_SCRATCH",
 }
+BWD_NOALLOC_MAX_ROWS = 1 << 22
 STATUS = {v: k for k, v in STATUS_NAMES.items()}
 
 # Every symbol the header declares.
@@ -34,6 +36,7 @@ EXPORTS = (
     "fa_fwd",
     "fa_bwd_workspace_bytes",
     "fa_bwd",
+    "fa_bwd_noalloc",
     "fa_bwd_dq",
     "fa_bwd_dkdv",
     "fa_dropout_mask",
@@ -72,6 +75,8 @@ def _declare(lib):
     lib.fa_bwd_workspace_bytes.argtypes = [P]
     lib.fa_bwd.restype = i32
     lib.fa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_noalloc.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fa_bwd_dq.restype = i32
     lib.fa_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_dkdv.restype = i32

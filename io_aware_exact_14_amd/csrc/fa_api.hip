@@ -5,9 +5,17 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_kernels.h"
+
+// Fixed device scratch of fa_bwd_noalloc: the D_i = dO_i . O_i rows of one
+// backward call (fp32 [B][H][N]). Each GPU the library runs on holds its own
+// copy from module load until the process ends. Host code never passes this
+// name to a kernel: in host code it is a stand-in, not a device address; the
+// device address comes from hipGetSymbolAddress (scratch_ptr below).
+__device__ __attribute__((aligned(256))) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
 
 namespace {
 
@@ -42,6 +50,30 @@ hipError_t device_topology(int& ncu, int& nxcd) {
     g_nxcd[dev].store(nxcd, std::memory_order_release);
     g_ncu[dev].store(ncu, std::memory_order_release);
   }
+  return hipSuccess;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each device holds its own copy at its own address).
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
   return hipSuccess;
 }
 
@@ -114,6 +146,7 @@ const char* fa_status_string(int s) {
     case FA_ERR_HIP: return "HIP runtime error at launch";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_RANGE: return "window outside [0, N) or (b, h) outside [0, B) x [0, H)";
+    case FA_ERR_SCRATCH: return "B*H*N exceeds the fixed scratch of fa_bwd_noalloc (FA_BWD_NOALLOC_MAX_ROWS)";
     default: return "unknown status";
   }
 }
@@ -189,6 +222,19 @@ int fa_bwd(const fa_params* p, const void* Q, const void* K, const void* V, cons
            const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, void* stream) {
   if (!dK || !dV) return FA_ERR_NULL;  // all three gradients are required here
   return bwd_stage(3, p, Q, K, V, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_noalloc(const fa_params* p, const void* Q, const void* K, const void* V, const void* O,
+                   const float* LSE, const void* dO, void* dQ, void* dK, void* dV, void* stream) {
+  const int st = check(p);
+  if (st != FA_OK) return st;
+  if (!Q || !K || !V || !O || !LSE || !dO || !dQ || !dK || !dV) return FA_ERR_NULL;
+  if (p->B * p->H * p->N > (int64_t)FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
+  if (p->B * p->H * p->N == 0) return FA_OK;
+  void* ws = nullptr;
+  if (scratch_ptr(&ws) != hipSuccess) return FA_ERR_HIP;
+  return bwd_stage(3, p, Q, K, V, O, LSE, dO, dQ, dK, dV, ws, sizeof(float) * (size_t)FA_BWD_NOALLOC_MAX_ROWS,
+                   stream);
 }
 
 int fa_bwd_dq(const fa_params* p, const void* Q, const void* K, const void* V, const void* O, const float* LSE,

@@ -116,6 +116,7 @@ def test_invalid_params_rejected(lib, L, kw, status):
     assert lib.fa_bwd(ctypes.byref(p), *([dummy] * 9), dummy, 1 << 30, None) == L.STATUS[status]
     assert lib.fa_bwd_dq(ctypes.byref(p), *([dummy] * 7), dummy, 1 << 30, None) == L.STATUS[status]
     assert lib.fa_bwd_dkdv(ctypes.byref(p), *([dummy] * 7), dummy, 1 << 30, None) == L.STATUS[status]
+    assert lib.fa_bwd_noalloc(ctypes.byref(p), *([dummy] * 9), None) == L.STATUS[status]
     assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 0
 
 
@@ -178,3 +179,24 @@ def test_empty_problem_is_a_no_op(lib, L):
     p = _params(L, N=0)
     assert lib.fa_fwd(ctypes.byref(p), 16, 16, 16, 16, 16, None) == 0
     assert lib.fa_bwd(ctypes.byref(p), *([16] * 9), None, 0, None) == 0
+
+
+def test_noalloc_entry_point_host_checks(lib, L):
+    # fa_bwd_noalloc rejects, before any HIP call: missing pointers, and
+    # B*H*N beyond its fixed scratch (FA_BWD_NOALLOC_MAX_ROWS fp32 rows)
+    header = open(os.path.join(ROOT, "include", "fa.h")).read()
+    assert "#define FA_BWD_NOALLOC_MAX_ROWS (1 << 22)" in header
+    assert L.BWD_NOALLOC_MAX_ROWS == 1 << 22
+    p = _params(L)
+    for i in range(9):  # Q, K, V, O, LSE, dO, dQ, dK, dV
+        args = [16] * 9
+        args[i] = None
+        assert lib.fa_bwd_noalloc(ctypes.byref(p), *args, None) == L.STATUS["FA_ERR_NULL"], i
+    assert lib.fa_bwd_noalloc(None, *([16] * 9), None) == L.STATUS["FA_ERR_NULL"]
+    big = _params(L, B=1, H=64, N=65537)  # 4194368 rows > 2^22
+    assert lib.fa_check_params(ctypes.byref(big)) == 0
+    assert lib.fa_bwd_noalloc(ctypes.byref(big), *([16] * 9), None) == L.STATUS["FA_ERR_SCRATCH"]
+    big2 = _params(L, B=4, H=16, N=65537, d=128)
+    assert lib.fa_bwd_noalloc(ctypes.byref(big2), *([16] * 9), None) == L.STATUS["FA_ERR_SCRATCH"]
+    # an empty problem is a no-op (no scratch lookup, nothing enqueued)
+    assert lib.fa_bwd_noalloc(ctypes.byref(_params(L, N=0)), *([16] * 9), None) == 0
