@@ -1,24 +1,29 @@
 #!/usr/bin/env python3
 """Throughput of tiled exact attention (forward + backward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --workload C2 --only           one workload (profiling runs)
     python bench.py --standard [--workload C2]     standard vs tiled attention
     python bench.py --sweep [--sweep-n 1024,...]   sequence-length sweep
+    python bench.py --roofs                        MFMA / exp / LDS / HBM microbenchmarks
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 fa_fwd (O, LSE), then the two backward stages fa_bwd_dq (D, dQ) and
 fa_bwd_dkdv (dK, dV), all through the C ABI on the current HIP stream.
-Inputs are resident in device memory before the timed region. The default
-workload is the GPT-2-medium attention layer (B=8, H=16, N=1024, d=64, bf16,
-causal). Prints ONE JSON line on stdout; per-kernel detail goes to stderr.
+Inputs are resident in device memory before the timed region. The headline
+workload is the long-context layer (B=1, H=32, N=16384, d=128, bf16,
+causal), the largest of the five; the same JSON line carries a `configs`
+entry for each of the five workloads (C1..C5), each with forward, backward
+and step TFLOP/s, MFMA fractions, warm and cache-flushed timings, per-kernel
+durations and the roofline of its dominant kernel. Prints ONE JSON line on
+stdout; progress goes to stderr.
 
 FLOP convention: forward 4*B*H*N^2*d (halved when causal, kept-block count
 when block-sparse), backward 2.5x forward.
 
-``--standard`` times the same workload through standard attention (every
-N x N intermediate written to device memory) beside the tiled kernels, and
-``--sweep`` times the tiled kernels and their device-memory footprint over
-sequence lengths; each prints one JSON line of its own.
+Per-kernel durations come from K back-to-back launches of one kernel between
+a single pair of HIP events on the launch stream, so they leave out the
+gaps between dependent kernels and sum to at most the step time.
 """
 from __future__ import annotations
 
@@ -112,9 +117,21 @@ def read_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(w, x, target_s=12.0):
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, x, target_s=20.0):
     """The fp64 oracle, as it stands, timed on the host over a bounded sample
-    of the workload's heads (forward + backward per head)."""
+    of the workload: whole (b, h) heads, each forward (oracle.forward_head)
+    then backward (oracle.backward_head), until about ``target_s`` seconds
+    have passed (at least one head). Rates follow the FLOP convention."""
     import numpy as np
 
     import oracle
@@ -127,28 +144,39 @@ def cpu_baseline(w, x, target_s=12.0):
         cores = len(os.sched_getaffinity(0))
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     bm = x["block_mask"]
-    done, t0 = 0, time.perf_counter()
+    done, t_fwd, t_bwd = 0, 0.0, 0.0
     for (b, h) in heads:
+        t0 = time.perf_counter()
         oracle.forward_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], w.scale, w.causal, w.dropout_p,
                             w.dropout_seed, b, h, bm, w.mask_block)
+        t1 = time.perf_counter()
         if w.backward:
             oracle.backward_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], x["do"][b, h], w.scale, w.causal,
                                  w.dropout_p, w.dropout_seed, b, h, bm, w.mask_block)
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_bwd += t2 - t1
         done += 1
-        if time.perf_counter() - t0 >= target_s:
+        if t_fwd + t_bwd >= target_s:
             break
-    dt = time.perf_counter() - t0
     kept = int(np.asarray(bm).sum()) if bm is not None else 0
     f, bwd = convention_flops(w, kept)
-    per_head = (f + bwd) / (w.B * w.H)
-    return {
-        "value": round(per_head * done / dt / 1e12, 6),
+    fh, bh = f / (w.B * w.H), bwd / (w.B * w.H)
+    out = {
+        "value": round((fh + bh) * done / (t_fwd + t_bwd) / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"{done} of {w.B * w.H} (b,h) heads of the same workload, fp64 numpy forward+backward "
-                  f"per head, {dt:.1f} s wall",
+        "sample": f"{done} of {w.B * w.H} (b,h) heads of {w.name}, fp64 numpy, each forward then backward; "
+                  f"{t_fwd:.1f} s forward + {t_bwd:.1f} s backward wall",
+        "cpu_model": _cpu_model(),
+        "host_threads_available": len(os.sched_getaffinity(0)),
+        "fwd_value": round(fh * done / t_fwd / 1e12, 6),
     }
+    if w.backward:
+        out["bwd_value"] = round(bh * done / t_bwd / 1e12, 6)
+        out["fwd_bwd_value"] = out["value"]
+    return out
 
 
 def standard_attention(q, k, v, do, scale, causal_mask=None):
@@ -426,19 +454,281 @@ def run_sweep(args):
     return 0
 
 
+
+
+# ---------------------------------------------------------------------------
+# the default run: the headline workload plus one entry per workload
+# ---------------------------------------------------------------------------
+class _Case:
+    """Device inputs, outputs and C-ABI launch closures of one workload."""
+
+    def __init__(self, w, dev, lib):
+        import numpy as np
+        import torch
+
+        import io_aware_exact_14_amd as fa
+        from workloads import workload_inputs
+
+        self.w = w
+        self.x = workload_inputs(w)
+        x = self.x
+        self.q, self.k, self.v = (x[n].to(dev) for n in ("q", "k", "v"))
+        self.do = x["do"].to(dev) if w.backward else None
+        bm = x["block_mask"]
+        self.kept = int(np.asarray(bm).sum()) if bm is not None else 0
+        self.bm_dev = torch.from_numpy(bm).to(dev) if bm is not None else None
+        self.grad_dtype = torch.float32
+        self.p = fa.params(w.B, w.H, w.N, w.d, w.torch_dtype, grad_dtype=self.grad_dtype, scale=w.scale,
+                           causal=w.causal, dropout_p=w.dropout_p, seed=w.dropout_seed, block_mask=self.bm_dev,
+                           mask_block=w.mask_block)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        if w.backward:
+            self.dq, self.dk, self.dv = (torch.empty(self.q.shape, dtype=self.grad_dtype, device=dev)
+                                         for _ in range(3))
+            self.ws = torch.empty(max(int(lib.fa_bwd_workspace_bytes(ctypes.byref(self.p))), 1), dtype=torch.uint8,
+                                  device=dev)
+        self.stream = torch.cuda.current_stream()
+        sp = ctypes.c_void_p(self.stream.cuda_stream)
+        pp = ctypes.byref(self.p)
+        fwd_args = (pp, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                    self.lse.data_ptr(), sp)
+        self.launch = {"fwd_kernel": lambda: lib.fa_fwd(*fwd_args)}
+        if w.backward:
+            dq_args = (pp, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                       self.lse.data_ptr(), self.do.data_ptr(), self.dq.data_ptr(), self.ws.data_ptr(),
+                       self.ws.numel(), sp)
+            dkdv_args = (pp, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.lse.data_ptr(),
+                         self.do.data_ptr(), self.dk.data_ptr(), self.dv.data_ptr(), self.ws.data_ptr(),
+                         self.ws.numel(), sp)
+            self.launch["bwd_dq_kernel"] = lambda: lib.fa_bwd_dq(*dq_args)
+            self.launch["bwd_dkdv_kernel"] = lambda: lib.fa_bwd_dkdv(*dkdv_args)
+        self.names = list(self.launch)
+
+    def step(self):
+        st = 0
+        for n in self.names:
+            st |= self.launch[n]()
+        if st != 0:
+            raise RuntimeError(f"libfa returned status {st} on {self.w.name}")
+
+
+def _roofline(w, model, kernel, avg_ms, peak_f):
+    flops_k, bytes_k = model[kernel]
+    sec = avg_ms * 1e-3
+    if flops_k / (peak_f * 1e12) >= bytes_k / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(flops_k / sec / 1e12, 3), "peak": peak_f, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(bytes_k / sec / 1e9, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 5)
+    roof["kernel"] = kernel
+    roof["kernel_avg_ms"] = round(avg_ms, 5)
+    roof["algorithmic_flops"] = flops_k
+    roof["compulsory_bytes"] = bytes_k
+    roof["traffic"] = read_traffic(kernel, w.name)
+    return roof
+
+
+def measure(case, steps, warmup, flush_buf, warm_ms=0.0):
+    """Warm whole steps by the host clock, per-kernel back-to-back durations
+    and cache-flushed steps (a 512 MiB write before each) by HIP events.
+
+    ``warmup`` steps run first; with ``warm_ms`` > 0, further untimed steps
+    run until that much device time has passed, since the GPU clock climbs
+    over the first tens of milliseconds of sustained load (the MFMA
+    microbenchmark of ``--roofs`` runs at ~1.8 GHz over 3 ms and ~2.3 GHz
+    over 23 ms)."""
+    import torch
+
+    w = case.w
+    for _ in range(warmup):
+        case.step()
+    if warm_ms > 0.0:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(case.stream)
+        case.step()
+        e1.record(case.stream)
+        torch.cuda.synchronize()
+        one = max(e0.elapsed_time(e1), 1e-3)
+        for _ in range(int(math.ceil(warm_ms / one))):
+            case.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        case.step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    # the same K back-to-back steps timed on the device (one event pair)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(case.stream)
+    for _ in range(steps):
+        case.step()
+    e1.record(case.stream)
+    torch.cuda.synchronize()
+    ms_step_dev = e0.elapsed_time(e1) / steps
+
+    per_kernel = {}
+    for n in case.names:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn = case.launch[n]
+        fn()
+        torch.cuda.synchronize()
+        e0.record(case.stream)
+        for _ in range(steps):
+            fn()
+        e1.record(case.stream)
+        torch.cuda.synchronize()
+        per_kernel[n] = e0.elapsed_time(e1) / steps
+    # leave the outputs of one whole, ordered step behind
+    case.step()
+
+    if flush_buf is None:
+        flushed = None
+    else:
+        flushed = []
+    for i in range(steps if flush_buf is not None else 0):
+        flush_buf.fill_(float(i & 7))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(case.stream)
+        case.step()
+        e1.record(case.stream)
+        torch.cuda.synchronize()
+        flushed.append(e0.elapsed_time(e1))
+    ms_flushed = sorted(flushed)[len(flushed) // 2] if flushed else None
+
+    el = torch.tensor([], dtype=w.torch_dtype).element_size()
+    model = kernel_model(w, case.kept, el, torch.tensor([], dtype=case.grad_dtype).element_size())
+    f_fwd, f_bwd = convention_flops(w, case.kept)
+    peak_f = PEAK_TFLOPS[w.dtype]
+    t_fwd = per_kernel["fwd_kernel"]
+    t_bwd = sum(per_kernel[n] for n in case.names[1:])
+    step_tf = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    entry = {
+        "workload": f"{w.name}: {WORKLOAD_TEXT[w.name]}",
+        "dtype": DTYPE_NAME[w.dtype],
+        "steps": steps,
+        "ms_per_step": round(ms_step, 5),
+        "ms_per_step_device_events": round(ms_step_dev, 5),
+        "tflops": round(step_tf, 3),
+        "mfma_frac": round(step_tf / peak_f, 5),
+        "fwd_tflops": round(f_fwd / (t_fwd * 1e-3) / 1e12, 3),
+        "fwd_mfma_frac": round(f_fwd / (t_fwd * 1e-3) / 1e12 / peak_f, 5),
+        "per_kernel": {n: {"avg_ms": round(per_kernel[n], 5),
+                           "tflops": round(model[n][0] / (per_kernel[n] * 1e-3) / 1e12, 3),
+                           "mfma_frac": round(model[n][0] / (per_kernel[n] * 1e-3) / 1e12 / peak_f, 5),
+                           "gbs": round(model[n][1] / (per_kernel[n] * 1e-3) / 1e9, 1)} for n in case.names},
+        "flushed": None if ms_flushed is None else {
+            "ms_per_step": round(ms_flushed, 5),
+            "tflops": round((f_fwd + f_bwd) / (ms_flushed * 1e-3) / 1e12, 3),
+            "method": "median of K steps, each after a 512 MiB device write, HIP events around the step"},
+    }
+    if w.backward:
+        entry["bwd_tflops"] = round(f_bwd / (t_bwd * 1e-3) / 1e12, 3)
+        entry["bwd_mfma_frac"] = round(f_bwd / (t_bwd * 1e-3) / 1e12 / peak_f, 5)
+    dom = max(case.names, key=lambda n: per_kernel[n])
+    entry["roofline"] = _roofline(w, model, dom, per_kernel[dom], peak_f)
+    return entry
+
+
+def run_main(args):
+    import torch
+
+    from io_aware_exact_14_amd import _lib
+    from workloads import WORKLOADS
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = _lib.load()
+    order = [args.workload] if args.only else [args.workload] + [n for n in sorted(WORKLOADS) if n != args.workload]
+    flush_buf = None if args.no_flush else torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    if args.copy_calibration:
+        src = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    entries = {}
+    head_case_x = None
+    for name in order:
+        w = WORKLOADS[name]
+        t0 = time.perf_counter()
+        case = _Case(w, dev, lib)
+        # the headline takes exactly --steps/--warmup; the small workloads take
+        # at least 100 steps so their microsecond kernels average over enough launches
+        is_head = name == args.workload
+        steps = args.steps if is_head else max(args.steps, 100 if w.N <= 1024 else args.steps)
+        entries[name] = measure(case, steps, args.warmup, flush_buf, 0.0 if is_head else args.warm_ms)
+        if name == args.workload:
+            head_case_x = case.x
+        print(f"[bench] {name}: {entries[name]['tflops']} TFLOP/s, step {entries[name]['ms_per_step']} ms "
+              f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+        del case
+        torch.cuda.empty_cache()
+    head = entries[args.workload]
+    w = WORKLOADS[args.workload]
+    result = {
+        "metric": METRIC,
+        "value": head["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {WORKLOAD_TEXT[w.name]}", "global_batch": w.B, "heads": w.H,
+                   "seq_len": w.N, "head_dim": w.d, "grad_dtype": "fp32", "parallelism": "none (1 GPU)"},
+        "mfma_frac": head["mfma_frac"],
+        "fwd_tflops": head["fwd_tflops"],
+        "fwd_mfma_frac": head["fwd_mfma_frac"],
+        "bwd_tflops": head.get("bwd_tflops"),
+        "bwd_mfma_frac": head.get("bwd_mfma_frac"),
+        "per_kernel": head["per_kernel"],
+        "flushed": head["flushed"],
+        "roofline": head["roofline"],
+        "configs": [entries[n] for n in sorted(entries)],
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, head_case_x)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_roofs(args):
+    """Microbenchmarks of the roofs the kernels are measured against (HIP
+    kernels in the package's roofs library): MFMA rate and the clock it runs
+    at, v_exp_f32 and fp32 FMA issue rates, LDS read bandwidth, HBM copy."""
+    import torch
+
+    from io_aware_exact_14_amd import roofs
+
+    torch.cuda.set_device(0)
+    out = roofs.run_all()
+    out["device"] = torch.cuda.get_device_name(0)
+    out["cus"] = torch.cuda.get_device_properties(0).multi_processor_count
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="C2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C4", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--only", action="store_true", help="measure --workload alone (no configs array)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache-flushed steps (profiling runs)")
+    ap.add_argument("--warm-ms", type=float, default=150.0,
+                    help="device time of untimed steps before timing each workload other than the headline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 512 MiB device copy first (reference kernel for HBM counters)")
-    ap.add_argument("--flush", action="store_true",
-                    help="also time K steps with a 512 MiB write before each, so no input is cached")
     ap.add_argument("--standard", action="store_true", help="standard vs tiled attention on --workload")
     ap.add_argument("--sweep", action="store_true", help="sequence-length sweep of the tiled kernels")
+    ap.add_argument("--roofs", action="store_true", help="MFMA / exp / LDS / HBM microbenchmarks")
     ap.add_argument("--sweep-n", default="1024,2048,4096,8192,16384,32768,65536")
     ap.add_argument("--sweep-d", default="64,128")
     ap.add_argument("--sweep-tokens", type=int, default=16384, help="B = max(1, tokens // N)")
@@ -450,160 +740,15 @@ def main():
         print("bench.py measures one GPU only: the attention path here is single-GPU "
               "(heads would shard over GPUs with no communication); run with --gpus 1", file=sys.stderr)
         return 2
+    if args.roofs:
+        return run_roofs(args)
     if args.standard:
+        if args.workload == "C4" and "--workload" not in " ".join(sys.argv):
+            args.workload = "C2"
         return run_standard(args)
     if args.sweep:
         return run_sweep(args)
-
-    import numpy as np
-    import torch
-
-    import io_aware_exact_14_amd as fa
-    from io_aware_exact_14_amd import _lib
-    from workloads import WORKLOADS, workload_inputs
-
-    w = WORKLOADS[args.workload]
-    x = workload_inputs(w)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
-    do = x["do"].to(dev) if w.backward else None
-    bm = x["block_mask"]
-    kept = int(np.asarray(bm).sum()) if bm is not None else 0
-    bm_dev = torch.from_numpy(bm).to(dev) if bm is not None else None
-    grad_dtype = torch.float32
-    p = fa.params(w.B, w.H, w.N, w.d, w.torch_dtype, grad_dtype=grad_dtype, scale=w.scale, causal=w.causal,
-                  dropout_p=w.dropout_p, seed=w.dropout_seed, block_mask=bm_dev, mask_block=w.mask_block)
-    lib = _lib.load()
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    if w.backward:
-        dq, dk, dv = (torch.empty(q.shape, dtype=grad_dtype, device=dev) for _ in range(3))
-        ws_n = int(lib.fa_bwd_workspace_bytes(ctypes.byref(p)))
-        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
-
-    if args.copy_calibration:
-        src = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    pp = ctypes.byref(p)
-    fwd_args = (pp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), sp)
-    if w.backward:
-        dq_args = (pp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                   dq.data_ptr(), ws.data_ptr(), ws.numel(), sp)
-        dkdv_args = (pp, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(), dk.data_ptr(),
-                     dv.data_ptr(), ws.data_ptr(), ws.numel(), sp)
-    names = ["fwd_kernel"] + (["bwd_dq_kernel", "bwd_dkdv_kernel"] if w.backward else [])
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        st = lib.fa_fwd(*fwd_args)
-        if ev is not None:
-            ev[1].record(stream)
-        if w.backward:
-            st |= lib.fa_bwd_dq(*dq_args)
-            if ev is not None:
-                ev[2].record(stream)
-            st |= lib.fa_bwd_dkdv(*dkdv_args)
-            if ev is not None:
-                ev[3].record(stream)
-        if st != 0:
-            raise RuntimeError(f"libfa returned status {st}")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: K whole steps, nothing recorded between the kernels.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # Per-kernel durations: K more steps with a HIP event pair around every
-    # launch on the launch stream (event markers add small gaps between the
-    # kernels, so this pass is kept out of the headline throughput).
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    kdur = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps for j, n in enumerate(names)}
-
-    flushed = None
-    if args.flush:
-        # Cold caches: a 512 MiB write (twice the 256 MB last-level cache)
-        # before every step, kept outside the HIP events around the kernels.
-        junk = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-        for i in range(args.steps):
-            junk.fill_(float(i))
-            step(fev[i])
-        torch.cuda.synchronize()
-        del junk
-        fdur = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in fev) / args.steps for j, n in enumerate(names)}
-        flushed = {"ms_per_step": round(sum(fdur.values()), 5),
-                   "per_kernel_ms": {n: round(fdur[n], 5) for n in names},
-                   "tflops": round((convention_flops(w, kept)[0] + convention_flops(w, kept)[1])
-                                   / (sum(fdur.values()) * 1e-3) / 1e12, 3)}
-    f_fwd, f_bwd = convention_flops(w, kept)
-    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
-
-    el = torch.tensor([], dtype=w.torch_dtype).element_size()
-    model = kernel_model(w, kept, el, torch.tensor([], dtype=grad_dtype).element_size())
-    dom = max(names, key=lambda n: kdur[n])
-    flops_k, bytes_k = model[dom]
-    peak_f = PEAK_TFLOPS[w.dtype]
-    t_mfma = flops_k / (peak_f * 1e12)
-    t_hbm = bytes_k / (PEAK_HBM_GBS * 1e9)
-    sec = kdur[dom] * 1e-3
-    if t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": round(flops_k / sec / 1e12, 3), "peak": peak_f, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(bytes_k / sec / 1e9, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 5)
-    roof["kernel"] = dom
-    roof["traffic"] = read_traffic(dom, w.name)
-
-    detail = {n: {"avg_ms": round(kdur[n], 5), "tflops": round(model[n][0] / (kdur[n] * 1e-3) / 1e12, 2),
-                  "mfma_frac": round(model[n][0] / (kdur[n] * 1e-3) / (peak_f * 1e12), 4),
-                  "gbs": round(model[n][1] / (kdur[n] * 1e-3) / 1e9, 1)} for n in names}
-    print(json.dumps({"per_kernel": detail, "fwd_tflops": round(f_fwd / (kdur["fwd_kernel"] * 1e-3) / 1e12, 2),
-                      "bwd_tflops": round(f_bwd / (sum(kdur[n] for n in names[1:]) * 1e-3) / 1e12, 2)
-                      if w.backward else None}), file=sys.stderr, flush=True)
-
-    result = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": DTYPE_NAME[w.dtype],
-        "data": "synthetic",
-        "config": {"workload": f"{w.name}: {WORKLOAD_TEXT[w.name]}", "global_batch": w.B, "heads": w.H,
-                   "seq_len": w.N, "head_dim": w.d, "grad_dtype": "fp32", "parallelism": "none (1 GPU)"},
-        "roofline": roof,
-    }
-    if flushed is not None:
-        result["flushed"] = flushed
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, x)
-    print(json.dumps(result), flush=True)
-    return 0
+    return run_main(args)
 
 
 if __name__ == "__main__":

@@ -5,7 +5,10 @@
 It never imports the package (whose import loads the library).
 
 Every .hip file under csrc/ is compiled to an object with hipcc, in
-parallel, then linked into io_aware_exact_14_amd/libfa.so. Packed fp32 VALU
+parallel, then linked into io_aware_exact_14_amd/libfa.so. The roofline
+microbenchmarks under roofs/ are built the same way into a library of their
+own, io_aware_exact_14_amd/libfa_roofs.so (measurement tooling for
+``bench.py --roofs``; the attention path never loads it). Packed fp32 VALU
 instructions are disabled for all device code.
 """
 from __future__ import annotations
@@ -24,6 +27,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+ROOFS_SRC = os.path.join(PKG, "roofs")
+ROOFS_LIB = os.path.join(PKG, "libfa_roofs.so")
 ARCH = "gfx950"
 
 
@@ -51,6 +56,33 @@ def _flags(resource_usage: bool):
     return f
 
 
+def _build_lib(cc, srcs, out, flags, verbose, jobs):
+    def compile_one(src):
+        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+        cmd = [cc, *flags, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        return src, obj, r
+
+    objs = []
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        for src, obj, r in ex.map(compile_one, srcs):
+            if verbose or r.returncode != 0:
+                msg = (r.stdout + r.stderr).strip()
+                msg = "\n".join(l for l in msg.splitlines() if "packed-fp32-ops" not in l)
+                if msg:
+                    print(f"== {os.path.basename(src)}\n{msg}", file=sys.stderr)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}")
+            objs.append(obj)
+    tmp = out + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = False, resource_usage: bool = False, jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
@@ -58,31 +90,11 @@ def build(verbose: bool = False, resource_usage: bool = False, jobs: int | None 
     if not srcs:
         raise RuntimeError("no HIP sources found")
     flags = _flags(resource_usage)
-
-    def compile_one(src):
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        cmd = [cc, *flags, "-c", src, "-o", obj]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        return src, obj, r
-
-    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
-    objs = []
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        for src, obj, r in ex.map(compile_one, srcs):
-            if verbose or r.returncode != 0:
-                out = (r.stdout + r.stderr).strip()
-                out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
-                if out:
-                    print(f"== {os.path.basename(src)}\n{out}", file=sys.stderr)
-            if r.returncode != 0:
-                raise RuntimeError(f"hipcc failed on {src}")
-            objs.append(obj)
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    jobs = jobs or min(len(srcs) + 1, max(1, (os.cpu_count() or 4)))
+    _build_lib(cc, srcs, LIB, flags, verbose, jobs)
+    roofs = sorted(glob.glob(os.path.join(ROOFS_SRC, "*.hip")))
+    if roofs:
+        _build_lib(cc, roofs, ROOFS_LIB, flags, verbose, jobs)
     return LIB
 
 

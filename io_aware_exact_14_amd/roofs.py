@@ -1,0 +1,84 @@
+"""Python driver of libfa_roofs.so: microbenchmarks of the roofs the
+attention kernels are measured against (bf16 MFMA rate and its clock,
+v_exp_f32 and fp32 FMA issue rates, LDS read bandwidth, HBM copy).
+
+Used by ``bench.py --roofs``. The library is built beside libfa.so by
+``build.py``; it is measurement tooling, not part of the attention path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_roofs.so")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise OSError(f"{LIB_PATH} is missing: build it with `python io_aware_exact_14_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    d = ctypes.POINTER(ctypes.c_double)
+    lib.roofs_mfma.argtypes = [ctypes.c_int, ctypes.c_int, d, d, d]
+    lib.roofs_valu.argtypes = [ctypes.c_int, ctypes.c_int, d, d, d]
+    lib.roofs_lds.argtypes = [ctypes.c_int, d, d, d]
+    lib.roofs_copy.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, d, d]
+    for f in (lib.roofs_mfma, lib.roofs_valu, lib.roofs_lds, lib.roofs_copy):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def _d():
+    return ctypes.c_double(0.0)
+
+
+def run_all(cus: int | None = None) -> dict:
+    """Runs every microbenchmark (one warm-up launch, then one timed launch
+    each). Cycle counts use the clock each kernel itself ran at."""
+    lib = _load()
+    if cus is None:
+        import torch
+
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"cus": cus}
+    for label, iters in (("short", 20000), ("long", 200000)):
+        tf, clk, ms = _d(), _d(), _d()
+        rc = lib.roofs_mfma(iters, 2, ctypes.byref(tf), ctypes.byref(clk), ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"roofs_mfma failed ({rc})")
+        out[f"mfma_bf16_tflops_{label}"] = round(tf.value, 2)
+        out[f"mfma_clock_ghz_{label}"] = round(clk.value, 4)
+        out[f"mfma_ms_{label}"] = round(ms.value, 3)
+        # 32x32x16 bf16 MFMA: 32768 flops per wave instruction, 4 SIMDs per CU
+        out[f"mfma_cycles_per_32x32x16_{label}"] = round(4 * cus * clk.value * 1e9 / (tf.value * 1e12 / 32768.0), 2)
+    for name, kind in (("exp", 0), ("fma", 1)):
+        r, clk, ms = _d(), _d(), _d()
+        rc = lib.roofs_valu(kind, 20000, ctypes.byref(r), ctypes.byref(clk), ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"roofs_valu({name}) failed ({rc})")
+        out[f"{name}_wave_inst_per_s"] = r.value
+        out[f"{name}_clock_ghz"] = round(clk.value, 4)
+        out[f"{name}_cycles_per_wave_inst"] = round(4 * cus * clk.value * 1e9 / r.value, 3)
+        out[f"{name}_ms"] = round(ms.value, 3)
+    r, clk, ms = _d(), _d(), _d()
+    if lib.roofs_lds(20000, ctypes.byref(r), ctypes.byref(clk), ctypes.byref(ms)) != 0:
+        raise RuntimeError("roofs_lds failed")
+    out["lds_read_b128_tb_s"] = round(r.value / 1e12, 3)
+    out["lds_clock_ghz"] = round(clk.value, 4)
+    out["lds_read_b128_bytes_per_clk_per_cu"] = round(r.value / (cus * clk.value * 1e9), 1)
+    out["lds_ms"] = round(ms.value, 3)
+    best = None
+    for bpc in (2, 8, 32):
+        for unr in (1, 4, 8):
+            r, ms = _d(), _d()
+            if lib.roofs_copy(1 << 30, bpc, unr, ctypes.byref(r), ctypes.byref(ms)) != 0:
+                raise RuntimeError("roofs_copy failed")
+            out[f"hbm_copy_gb_s_wg{bpc}_unr{unr}"] = round(r.value / 1e9, 1)
+            if best is None or r.value > best:
+                best = r.value
+    out["hbm_copy_gb_s_best"] = round(best / 1e9, 1)
+    out["notes"] = ("MFMA: v_mfma_f32_32x32x16_bf16, 2 waves per SIMD x 4 independent chains, 20000 and 200000 "
+                    "iterations. Clocks: s_memtime over s_memrealtime on wave 0 of each kernel. exp/fma: 8 "
+                    "independent chains per lane, 4 waves per SIMD. LDS: ds_read_b128, consecutive 16-byte chunks "
+                    "per wave, 4 waves per SIMD. HBM: 1 GiB device copy (read + write bytes counted), nontemporal "
+                    "loads and stores, workgroups per CU x 16-byte elements per lane per step swept.")
+    return out

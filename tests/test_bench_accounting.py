@@ -82,3 +82,25 @@ def test_traffic_is_tied_to_the_kernel_sources(monkeypatch, tmp_path):
     assert bench.read_traffic("bwd_dq_kernel", "C2") is None  # no summary
     f.write_text("src_sha256: " + "0" * 64 + "\ntraffic_bytes_per_dispatch: 146779177\n")
     assert bench.read_traffic("bwd_dkdv_kernel", "C2") is None  # stale summary
+
+
+def test_roofline_picks_the_binding_roof_and_reports_the_ratio():
+    # C4 dK/dV: 4.398 TFLOP of algorithmic work against 1.08 GB compulsory:
+    # MFMA-bound; achieved = flops / time, frac = achieved / 2500
+    w = WORKLOADS["C4"]
+    m = bench.kernel_model(w, 0, 2, 4)
+    r = bench._roofline(w, m, "bwd_dkdv_kernel", 4.0, 2500.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["achieved"] == pytest.approx(4.398046511104e12 / 4e-3 / 1e12, rel=1e-6)
+    assert r["frac"] == pytest.approx(r["achieved"] / 2500.0, rel=1e-4)
+    # C2 dK/dV: 135.3 MB in 50 us is above the MFMA time of its 34.4 GFLOP: HBM-bound
+    w2 = WORKLOADS["C2"]
+    r2 = bench._roofline(w2, bench.kernel_model(w2, 0, 2, 4), "bwd_dkdv_kernel", 0.05, 2500.0)
+    assert r2["bound"] == "hbm" and r2["unit"] == "GB/s"
+    assert r2["achieved"] == pytest.approx(135.3e6 / 50e-6 / 1e9, rel=2e-3)
+
+
+def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    assert bench.main() == 2
+    assert "one GPU" in capsys.readouterr().err
