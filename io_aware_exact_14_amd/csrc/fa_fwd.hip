@@ -416,6 +416,212 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   }
 }
 
+// Split-key forward for grids too small to fill the device (few heads and
+// short sequences: one 128-row tile per head would leave most CUs idle and
+// give each wave a long serial chain of MFMAs). A workgroup owns 32 query
+// rows; its four waves take the key tiles j = w, w + 4, ... (32 keys each,
+// so causal work spreads evenly), each with its own LDS tile and its own
+// running maximum and sum, and the four partial results are merged in LDS
+// at the end with the same rescaling the online softmax uses between tiles
+// (FlashAttention milestone page, "The idea": two running numbers per row,
+// partial results rescaled to a common maximum).
+template <typename T, int D>
+struct SplitCfg {
+  static constexpr int BC = 32;                             // keys per wave tile
+  static constexpr int EPC = 16 / sizeof(T);                // elements per 16-byte chunk
+  static constexpr int KS = D + (sizeof(T) == 2 ? (D == 128 ? 24 : 8) : 4);  // padded LDS row (elements)
+  static constexpr int KCH = D / EPC;                       // 16-byte chunks per row
+  static constexpr int NLD = BC * KCH / 64;                 // 16-byte loads per lane per tensor per tile
+  static constexpr int TILE = BC * KS;                      // elements per K (or V) tile
+  static constexpr int OS = D + 4;                          // fp32 row stride of the partial O
+  static constexpr int TILE_BYTES = 4 * 2 * TILE * (int)sizeof(T);
+  static constexpr int COMB_BYTES = 4 * 32 * OS * 4;
+  static constexpr int BYTES = TILE_BYTES > COMB_BYTES ? TILE_BYTES : COMB_BYTES;
+};
+
+template <typename T, int D, bool DROP>
+__global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
+  using C = SplitCfg<T, D>;
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr int KI = M::KI, KH = M::KH;
+  constexpr int BC = C::BC, NDB = D / 32, NC = D / KI;
+  constexpr int RB = D * (int)sizeof(T);
+  constexpr float NEG_INF = -__builtin_inff();
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::BYTES];
+  __shared__ float ms[4][32], ls[4][32], mrow[32], lrow[32];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, lo = lane & 31, hi = lane >> 5;
+  const int N = a.N;
+  const int nq = (N + 31) / 32;
+  const int rank = blockIdx.x / a.BH;
+  const int bh = blockIdx.x - rank * a.BH;
+  const int qt = a.causal ? (nq - 1 - rank) : rank;  // causal: longest rows first
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const T* __restrict__ Kg = static_cast<const T*>(a.k) + hoff;
+  const T* __restrict__ Vg = static_cast<const T*>(a.v) + hoff;
+  const int q0 = qt * 32;
+  const int q = q0 + lo;
+
+  const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(static_cast<const T*>(a.q) + hoff, N * RB);
+  frag qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if constexpr (KH == 8)
+      qf[c] = __builtin_bit_cast(frag, buffer_load16(qrs, q * RB + (c * KI + hi * KH) * (int)sizeof(T)));
+    else
+      qf[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qrs, q * RB + (c * KI + hi) * 4, 0, 0));
+  }
+  uint32_t rowhash = 0;
+  if constexpr (DROP) {
+    const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
+    rowhash = fmix32(hk ^ (uint32_t)q) + (uint32_t)(2 * hi);  // crow's 4*hi keys = 2*hi pairs
+  }
+
+  const int kend = a.causal ? min(N, q0 + 32) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+  const uint8_t* bmrow = a.bmask ? a.bmask + (size_t)(q0 / a.mask_block) * a.nb : nullptr;
+
+  T* Ks = reinterpret_cast<T*>(smem) + w * 2 * C::TILE;  // this wave's K tile, then its V tile
+  T* Vs = Ks + C::TILE;
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = zero16();
+  float m_run = NEG_INF, l_run = 0.f;
+
+  for (int j = w; j < ntiles; j += 4) {
+    if (bmrow != nullptr && !mask_kept(bmrow, (j * BC) / a.mask_block)) continue;
+    const int k0 = j * BC;
+    // The wave loads its own tile (rows past the end read as zeros). LDS
+    // operations of one wave run in order, so these stores follow the reads
+    // of the previous tile and precede this tile's reads.
+    {
+      const int rem = (N - k0) * RB;
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (size_t)k0 * D, rem);
+      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (size_t)k0 * D, rem);
+      u32x4 kreg[C::NLD], vreg[C::NLD];
+#pragma unroll
+      for (int i = 0; i < C::NLD; ++i) {
+        const int c = i * 64 + lane;
+        const int off = (c / C::KCH) * RB + (c % C::KCH) * 16;
+        kreg[i] = buffer_load16(kr, off);
+        vreg[i] = buffer_load16(vr, off);
+      }
+#pragma unroll
+      for (int i = 0; i < C::NLD; ++i) {
+        const int c = i * 64 + lane;
+        const int e = (c / C::KCH) * C::KS + (c % C::KCH) * C::EPC;
+        *reinterpret_cast<u32x4*>(&Ks[e]) = kreg[i];
+        *reinterpret_cast<u32x4*>(&Vs[e]) = vreg[i];
+      }
+    }
+    f32x16 sc = zero16();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sc = M::run(load_frag<T>(Ks + lo * C::KS + c * KI + hi * KH), qf[c], sc);
+    if ((a.causal && k0 + BC - 1 > q0) || (k0 + BC > N)) {
+      const int t = (a.causal ? min(q, N - 1) : N - 1) - k0 - 4 * hi;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (8 * (v >> 2) + (v & 3) > t) sc[v] = NEG_INF;
+    }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+    mx = half_max(mx);
+    const float mnew = fmaxf(m_run, mx * a.sl2);
+    if (wave_any(mnew > m_run + kLazyRescale)) {
+      const float alpha = exp2_fast(m_run - (mnew == NEG_INF ? 0.f : mnew));
+      m_run = mnew;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    }
+    const float base = (m_run == NEG_INF) ? 0.f : m_run;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float pv = exp2_fast(fmaf(sc[v], a.sl2, -base));
+      l_run += pv;
+      sc[v] = pv;
+    }
+    if constexpr (DROP) {
+      const uint32_t y = (rowhash + (uint32_t)(k0 >> 1)) * kMixMul;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const uint32_t u = keep_finish(y + (uint32_t)(4 * (v >> 2) + ((v & 3) >> 1)) * kMixMul);
+        sc[v] = keep_lo(u, a.thresh) ? sc[v] : 0.f;
+        sc[v + 1] = keep_hi(u, a.thresh) ? sc[v + 1] : 0.f;
+      }
+    }
+    if constexpr (KH == 8) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const frag pb = pack8<T>(sc[8 * hf + 0], sc[8 * hf + 1], sc[8 * hf + 2], sc[8 * hf + 3], sc[8 * hf + 4],
+                                 sc[8 * hf + 5], sc[8 * hf + 6], sc[8 * hf + 7]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = M::run(load_frag_tr<T>(Vs, C::KS, 16 * hf, db * 32, lane), pb, o[db]);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = crow(v, hi);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = M::run(Vs[kk * C::KS + db * 32 + lo], sc[v], o[db]);
+      }
+    }
+  }
+
+  // Merge the four waves' partial results: M = max_w m_w, a_w = 2^(m_w - M),
+  // L = sum_w a_w l_w, O = sum_w a_w O_w / L.
+  const float lt = half_sum(l_run);
+  if (hi == 0) {
+    ms[w][lo] = m_run;
+    ls[w][lo] = lt;
+  }
+  __syncthreads();  // every wave is done with its tile and has posted its row statistics
+  float mall = NEG_INF;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) mall = fmaxf(mall, ms[x][lo]);
+  const float aw = (m_run == NEG_INF) ? 0.f : exp2_fast(m_run - mall);
+  float* Os = reinterpret_cast<float*>(smem) + w * 32 * C::OS;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = {o[db][4 * g] * aw, o[db][4 * g + 1] * aw, o[db][4 * g + 2] * aw, o[db][4 * g + 3] * aw};
+      *reinterpret_cast<f32x4*>(&Os[lo * C::OS + db * 32 + 8 * g + 4 * hi]) = x;
+    }
+  if (w == 0 && hi == 0) {
+    float L = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) L += ms[x][lo] == NEG_INF ? 0.f : ls[x][lo] * exp2_fast(ms[x][lo] - mall);
+    mrow[lo] = mall;
+    lrow[lo] = L;
+  }
+  __syncthreads();
+  const float* O0 = reinterpret_cast<const float*>(smem);
+  T* __restrict__ Og = static_cast<T*>(a.out) + hoff;
+  constexpr int C4 = D / 4;  // groups of 4 columns per row
+  for (int idx = tid; idx < 32 * C4; idx += 256) {
+    const int r = idx / C4, c = (idx % C4) * 4;
+    if (q0 + r >= N) continue;
+    const float L = lrow[r];
+    const float inv = L > 0.f ? a.rp / L : 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc += *reinterpret_cast<const f32x4*>(&O0[(x * 32 + r) * C::OS + c]);
+    store4<T>(Og + (size_t)(q0 + r) * D + c, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  }
+  if (tid < 32 && q0 + tid < N) {
+    const float L = lrow[tid];
+    a.lse[(size_t)bh * N + q0 + tid] = L > 0.f ? (mrow[tid] + log2_fast(L)) * kLn2 : NEG_INF;
+  }
+}
+
 // Resident waves per SIMD: with one wave, softmax VALU work, LDS reads and
 // MFMAs of a tile run back to back; more waves let them overlap. d = 128
 // fits two waves (256 VGPRs, two workgroups' LDS in the 160 KB of a CU);
@@ -430,8 +636,23 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// A grid of 128-row tiles that would occupy at most a quarter of the CUs
+// takes the split-key kernel instead: four times the workgroups, each wave a
+// quarter of the keys.
+template <typename T, int D>
+static hipError_t launch_fwd_split(bool dropout, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(((a.N + 31) / 32) * a.BH));
+  if (dropout)
+    fwd_split_kernel<T, D, true><<<grid, dim3(256), 0, s>>>(a);
+  else
+    fwd_split_kernel<T, D, false><<<grid, dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int BC, int QB>
 static hipError_t launch_fwd_d(bool dropout, const AttnArgs& a, hipStream_t s) {
+  const long tiles = (long)((a.N + 127) / 128) * a.BH;
+  if (4 * tiles <= a.ncu) return launch_fwd_split<T, D>(dropout, a, s);
   return dropout ? launch_fwd_t<T, D, BC, QB, true>(a, s) : launch_fwd_t<T, D, BC, QB, false>(a, s);
 }
 
