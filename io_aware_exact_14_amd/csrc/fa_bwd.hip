@@ -44,19 +44,21 @@ struct TileShape {
   // than the register-staged loads.
   static constexpr bool DMA = USE_DMA && sizeof(T) == 2 && D == 128;
   static constexpr int RS = DMA ? D : KS;                   // tile row stride (elements)
-  // Element (row, col) of a streamed tile; col is a multiple of 4.
+  // Element (row, col) of a streamed tile; col is a multiple of 4. Padded
+  // tiles store tile row r at LDS row lds_row(r) (conflict-free transpose
+  // reads); swizzled tiles keep rows in place and move 16-byte chunks.
   static __device__ __forceinline__ int at(int row, int col) {
     if constexpr (DMA)
       return row * D + (((col / EPC) ^ lds_swizzle<D>(row)) * EPC) + (col % EPC);
     else
-      return row * KS + col;
+      return lds_row(row) * KS + col;
   }
   // Transposed fragment (load_frag_tr) of a streamed tile.
   static __device__ __forceinline__ typename Mfma<T>::frag tr(const T* tile, int base, int col0, int lane) {
     if constexpr (DMA)
       return load_frag_tr_swz<T, D>(tile, base, col0, lane);
     else
-      return load_frag_tr<T>(tile, KS, base, col0, lane);
+      return load_frag_tr_rp<T>(tile, KS, base, col0, lane);
   }
 };
 
@@ -160,7 +162,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
     for (int i = 0; i < (S::DMA ? 1 : NLD); ++i) {
       const int c = i * 256 + tid;
-      const int row = c / S::KCH, ch = c % S::KCH;
+      const int row = lds_row(c / S::KCH), ch = c % S::KCH;
       *reinterpret_cast<u32x4*>(&smem[buf][row * S::KS + ch * S::EPC]) = kreg[i];
       *reinterpret_cast<u32x4*>(&smem[buf][TILE + row * S::KS + ch * S::EPC]) = vreg[i];
     }
@@ -266,9 +268,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int kl = kb * 32 + crow(v, hi);
+            const int kl = S::at(kb * 32 + crow(v, hi), 0);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) dq[db] = M::run(Ks[kl * S::RS + db * 32 + lo], s[kb][v], dq[db]);
+            for (int db = 0; db < NDB; ++db) dq[db] = M::run(Ks[kl + db * 32 + lo], s[kb][v], dq[db]);
           }
       }
     }
@@ -437,7 +439,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int c = i * 256 + tid;
-      const int row = c / S::KCH, ch = c % S::KCH;
+      const int row = lds_row(c / S::KCH), ch = c % S::KCH;
       *reinterpret_cast<u32x4*>(&smem[buf][row * S::KS + ch * S::EPC]) = qreg[i];
       *reinterpret_cast<u32x4*>(&smem[buf][TILE + row * S::KS + ch * S::EPC]) = oreg[i];
     }
@@ -575,11 +577,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int ql = qb * 32 + crow(v, hi);
+            const int ql = S::at(qb * 32 + crow(v, hi), 0);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-              dv[db] = M::run(dOs[ql * S::RS + db * 32 + lo], s[qb][v], dv[db]);
-              dk[db] = M::run(Qs[ql * S::RS + db * 32 + lo], dp[qb][v], dk[db]);
+              dv[db] = M::run(dOs[ql + db * 32 + lo], s[qb][v], dv[db]);
+              dk[db] = M::run(Qs[ql + db * 32 + lo], dp[qb][v], dk[db]);
             }
           }
       }

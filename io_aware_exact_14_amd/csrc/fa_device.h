@@ -176,6 +176,34 @@ __device__ __forceinline__ typename Mfma<T>::frag load_frag_tr(const T* tile, in
   return __builtin_bit_cast(typename Mfma<T>::frag, xy);
 }
 
+// Row permutation of the padded (register-staged) LDS tiles: tile row r is
+// stored at LDS row lds_row(r), which swaps bits 0-1 and 2-3 of r. A
+// transpose read gathers 4 tile rows 4*x + {0,1,2,3} (the k order of the
+// accumulator tile, crow) and each half-wave reads 64 bytes of each; at the
+// padded strides (36 dwords at d = 64, 76 at d = 128, both 4 x odd) those
+// rows sit 12 or 36 dwords apart mod 64 banks, so their 16-dword windows
+// overlap (2-way conflicts). Permuted, the 4 rows are LDS rows y + 4e, 4*9 or
+// 4*19 dwords apart per step, i.e. 16-dword windows at 0, 16, 32, 48 mod 64:
+// disjoint. 16-byte row reads of 16 consecutive tile rows still hit 16
+// distinct bank quads (lds_row permutes each group of 16 rows).
+__device__ __forceinline__ constexpr int lds_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// load_frag_tr over a tile whose rows are stored at lds_row(r): the rows
+// base + 4*(l/32) + {0..3} (and + 8) of the fragment sit at LDS rows
+// base + 4*{0..3} + l/32 (and + 2). base must be a multiple of 16.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag load_frag_tr_rp(const T* tile, int stride, int base, int col0,
+                                                                   int lane) {
+  static_assert(sizeof(T) == 2, "16-bit only");
+  const int j = lane & 15;
+  const T* p = tile + (base + 4 * (j >> 2) + (lane >> 5)) * stride + col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 2 * stride));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 xy = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(typename Mfma<T>::frag, xy);
+}
+
 // XOR swizzle (in 16-byte chunks) of an unpadded 16-bit LDS tile row of D
 // elements: the logical chunk lc of row r sits at physical chunk
 // lc ^ lds_swizzle<D>(r). With 64 banks of 4 bytes, it keeps both read

@@ -177,7 +177,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
     for (int i = 0; i < (C::DMA ? 1 : C::NLD); ++i) {
       const int c = i * 256 + tid;
-      const int row = c / C::KCH, ch = c % C::KCH;
+      const int row = lds_row(c / C::KCH), ch = c % C::KCH;
       *reinterpret_cast<u32x4*>(&smem[buf][row * C::KS + ch * C::EPC]) = kreg[i];
       *reinterpret_cast<u32x4*>(&smem[buf][C::TILE + row * C::KS + ch * C::EPC]) = vreg[i];
     }
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             const int row = kb * 32 + lo;
             kf = load_frag<T>(Ks + row * D + (((c * KI + hi * KH) / C::EPC) ^ lds_swizzle<D>(row)) * C::EPC);
           } else {
-            kf = load_frag<T>(Ks + (kb * 32 + lo) * C::KS + c * KI + hi * KH);
+            kf = load_frag<T>(Ks + lds_row(kb * 32 + lo) * C::KS + c * KI + hi * KH);
           }
 #pragma unroll
           for (int b = 0; b < QB; ++b) s[b][kb] = M::run(kf, qf[b][c], s[b][kb]);
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
               if constexpr (C::DMA)
                 vt = load_frag_tr_swz<T, D>(Vs, kb * 32 + 16 * hf, db * 32, lane);
               else
-                vt = load_frag_tr<T>(Vs, C::KS, kb * 32 + 16 * hf, db * 32, lane);
+                vt = load_frag_tr_rp<T>(Vs, C::KS, kb * 32 + 16 * hf, db * 32, lane);
 #pragma unroll
               for (int b = 0; b < QB; ++b) o[b][db] = M::run(vt, pb[b], o[b][db]);
             }
@@ -334,7 +334,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int kk = kb * 32 + crow(v, hi);
+            const int kk = lds_row(kb * 32 + crow(v, hi));
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
               const float vt = Vs[kk * C::KS + db * 32 + lo];
@@ -513,14 +513,14 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < C::NLD; ++i) {
         const int c = i * 64 + lane;
-        const int e = (c / C::KCH) * C::KS + (c % C::KCH) * C::EPC;
+        const int e = lds_row(c / C::KCH) * C::KS + (c % C::KCH) * C::EPC;
         *reinterpret_cast<u32x4*>(&Ks[e]) = kreg[i];
         *reinterpret_cast<u32x4*>(&Vs[e]) = vreg[i];
       }
     }
     f32x16 sc = zero16();
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sc = M::run(load_frag<T>(Ks + lo * C::KS + c * KI + hi * KH), qf[c], sc);
+    for (int c = 0; c < NC; ++c) sc = M::run(load_frag<T>(Ks + lds_row(lo) * C::KS + c * KI + hi * KH), qf[c], sc);
     if ((a.causal && k0 + BC - 1 > q0) || (k0 + BC > N)) {
       const int t = (a.causal ? min(q, N - 1) : N - 1) - k0 - 4 * hi;
 #pragma unroll
@@ -563,12 +563,12 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
         const frag pb = pack8<T>(sc[8 * hf + 0], sc[8 * hf + 1], sc[8 * hf + 2], sc[8 * hf + 3], sc[8 * hf + 4],
                                  sc[8 * hf + 5], sc[8 * hf + 6], sc[8 * hf + 7]);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] = M::run(load_frag_tr<T>(Vs, C::KS, 16 * hf, db * 32, lane), pb, o[db]);
+        for (int db = 0; db < NDB; ++db) o[db] = M::run(load_frag_tr_rp<T>(Vs, C::KS, 16 * hf, db * 32, lane), pb, o[db]);
       }
     } else {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int kk = crow(v, hi);
+        const int kk = lds_row(crow(v, hi));
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] = M::run(Vs[kk * C::KS + db * 32 + lo], sc[v], o[db]);
       }
