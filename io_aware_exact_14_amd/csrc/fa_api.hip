@@ -121,6 +121,7 @@ fa::AttnArgs make_args(const fa_params* p) {
   a.thresh = (uint32_t)std::floor(p->dropout_p * 65536.0) << 16;
   a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFu);
   a.seed_hi = (uint32_t)(p->seed >> 32);
+  a.ones16 = 0x00010001u;
   return a;
 }
 
@@ -165,9 +166,10 @@ int fa_fwd(const fa_params* p, const void* Q, const void* K, const void* V, void
   a.v = V;
   a.out = O;
   a.lse = LSE;
-  // Any p > 0 takes the dropout kernels, even when floor(p * 2^32) is 0 and
-  // every element is kept: the output is still scaled by 1 / (1 - p).
-  const bool dropout = p->dropout_p > 0.0;
+  // The dropout kernels draw keep bits only when some key can be dropped
+  // (T16 = floor(p * 2^16) >= 1). Below that every key is kept and the plain
+  // kernel computes the same output: its epilogue scales by 1 / (1 - p) too.
+  const bool dropout = a.thresh != 0;
   hipError_t e = prepare_launch(a);
   if (e == hipSuccess) e = fa::launch_fwd(elt(p->in_dtype), (int)p->d, dropout, a, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

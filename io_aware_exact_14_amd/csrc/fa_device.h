@@ -104,6 +104,7 @@ __device__ __forceinline__ typename Mfma<T>::frag pack8(float x0, float x1, floa
 
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -139,6 +140,19 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t x) { return keep_finish((x ^
 // With thresh = T16 << 16 (T16 = floor(p * 2^16)): the high half is kept iff
 // u >= thresh, the low half iff (u << 16) >= thresh.
 __device__ __forceinline__ bool keep_hi(uint32_t u, uint32_t thresh) { return u >= thresh; }
+
+// The same decisions for both keys of a pair at once, on the word's two
+// 16-bit halves as packed integers: half >= T16 <=> sat(half - (T16 - 1)) >= 1,
+// so min(sat(half - tm1), 1) is 1 for a kept key and 0 for a dropped one
+// (tm1 = T16 - 1 in both halves; T16 >= 1). Multiplying the bits of a
+// packed 16-bit pair of P by it keeps or zeroes each value exactly.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+// `ones` is {1, 1} passed at run time (AttnArgs::ones16): with a literal 1
+// the compiler rewrites the min into two compares and selects.
+__device__ __forceinline__ u16x2 keep01(uint32_t u, u16x2 tm1, u16x2 ones) {
+  return __builtin_elementwise_min(__builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, u), tm1), ones);
+}
 __device__ __forceinline__ bool keep_lo(uint32_t u, uint32_t thresh) { return (u << 16) >= thresh; }
 
 // Per-(b, h) dropout key from the 64-bit seed.

@@ -288,11 +288,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
           }
         l_run[b] += rs;
 
-        if constexpr (DROP) {
+        if constexpr (DROP && KH != 8) {
           // Keys k0 + kb*32 + crow(v, hi); elements v and v + 1 (v even) are
           // the two keys of pair k0/2 + kb*16 + 4*(v/4) + 2*hi + (v%4)/2: one
           // product per tile, then a constant per pair (keep_finish) whose
-          // low half decides the even key and high half the odd one.
+          // low half decides the even key and high half the odd one. (The
+          // 16-bit path applies the same bits to packed P below.)
           const uint32_t y = (rowhash[b] + (uint32_t)(k0 >> 1)) * kMixMul;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
@@ -309,15 +310,38 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
       // O^T += V^T P^T: P^T is the B operand straight from registers; V^T
       // comes from the row-major V tile through LDS transpose reads.
       if constexpr (KH == 8) {
+        // Dropout on the packed P: the 16-bit values of a dword are the two
+        // keys of one pair (elements 8*hf + 2e, + 1: pair k0/2 + kb*16 +
+        // 8*hf + {0, 1, 4, 5}[e] + 2*hi), so the pair's keep word zeroes them
+        // with packed integer ops (keep01). The host never launches the
+        // dropout kernels with T16 = 0 (every key kept: the plain kernel,
+        // whose epilogue applies 1 / (1 - p) too).
+        const u16x2 tm1 = {(unsigned short)((a.thresh >> 16) - 1u), (unsigned short)((a.thresh >> 16) - 1u)};
+        const u16x2 ones = __builtin_bit_cast(u16x2, a.ones16);
+        uint32_t ytile[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) ytile[b] = DROP ? (rowhash[b] + (uint32_t)(k0 >> 1)) * kMixMul : 0u;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
             frag pb[QB];
 #pragma unroll
-            for (int b = 0; b < QB; ++b)
+            for (int b = 0; b < QB; ++b) {
               pb[b] = pack8<T>(s[b][kb][8 * hf + 0], s[b][kb][8 * hf + 1], s[b][kb][8 * hf + 2], s[b][kb][8 * hf + 3],
                                s[b][kb][8 * hf + 4], s[b][kb][8 * hf + 5], s[b][kb][8 * hf + 6], s[b][kb][8 * hf + 7]);
+              if constexpr (DROP) {
+                u16x8 km;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const uint32_t off = (uint32_t)(kb * 16 + 8 * hf + 4 * (e >> 1) + (e & 1));
+                  const u16x2 k2 = keep01(keep_finish(ytile[b] + off * kMixMul), tm1, ones);
+                  km[2 * e] = k2[0];
+                  km[2 * e + 1] = k2[1];
+                }
+                pb[b] = __builtin_bit_cast(frag, __builtin_bit_cast(u16x8, pb[b]) * km);
+              }
+            }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
               frag vt;
@@ -548,8 +572,8 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
       l_run += pv;
       sc[v] = pv;
     }
-    if constexpr (DROP) {
-      const uint32_t y = (rowhash + (uint32_t)(k0 >> 1)) * kMixMul;
+    const uint32_t y = DROP ? (rowhash + (uint32_t)(k0 >> 1)) * kMixMul : 0u;
+    if constexpr (DROP && KH != 8) {
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
         const uint32_t u = keep_finish(y + (uint32_t)(4 * (v >> 2) + ((v & 3) >> 1)) * kMixMul);
@@ -558,10 +582,22 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
       }
     }
     if constexpr (KH == 8) {
+      const u16x2 tm1 = {(unsigned short)((a.thresh >> 16) - 1u), (unsigned short)((a.thresh >> 16) - 1u)};
+      const u16x2 ones = __builtin_bit_cast(u16x2, a.ones16);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const frag pb = pack8<T>(sc[8 * hf + 0], sc[8 * hf + 1], sc[8 * hf + 2], sc[8 * hf + 3], sc[8 * hf + 4],
-                                 sc[8 * hf + 5], sc[8 * hf + 6], sc[8 * hf + 7]);
+        frag pb = pack8<T>(sc[8 * hf + 0], sc[8 * hf + 1], sc[8 * hf + 2], sc[8 * hf + 3], sc[8 * hf + 4],
+                           sc[8 * hf + 5], sc[8 * hf + 6], sc[8 * hf + 7]);
+        if constexpr (DROP) {  // packed keep factors, as in the 128-row kernel (T16 >= 1)
+          u16x8 km;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u16x2 k2 = keep01(keep_finish(y + (uint32_t)(8 * hf + 4 * (e >> 1) + (e & 1)) * kMixMul), tm1, ones);
+            km[2 * e] = k2[0];
+            km[2 * e + 1] = k2[1];
+          }
+          pb = __builtin_bit_cast(frag, __builtin_bit_cast(u16x8, pb) * km);
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] = M::run(load_frag_tr_rp<T>(Vs, C::KS, 16 * hf, db * 32, lane), pb, o[db]);
       }

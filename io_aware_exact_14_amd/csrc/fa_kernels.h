@@ -37,6 +37,8 @@ struct AttnArgs {
                      // 16-bit half of the keep word, moved to the top bits, is >= thresh
   uint32_t seed_lo;
   uint32_t seed_hi;
+  uint32_t ones16;   // 0x00010001: packed 16-bit ones (a runtime value, so that the packed
+                     // keep-factor arithmetic stays packed instead of becoming compares)
   int ncu;           // compute units of the device the call runs on
   int nxcd;          // accelerator complex dies (XCDs) among which workgroup ids are dealt
 };
