@@ -139,7 +139,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int kend = a.causal ? min(N, qtile0 + BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
   const uint8_t* bmrow = a.bmask ? a.bmask + (size_t)(qtile0 / a.mask_block) * a.nb : nullptr;
-  auto kept = [&](int j) { return bmrow == nullptr || mask_kept(bmrow, (j * BC) / a.mask_block); };
+  const bool mfew = bmrow != nullptr && a.nb <= 64;  // the row's mask fits one 64-bit word
+  const uint64_t mrow = mfew ? mask_bits(bmrow, 1, a.nb, lane) : ~0ull;
+  auto kept = [&](int j) {
+    if (bmrow == nullptr) return true;
+    const int blk = (j * BC) / a.mask_block;
+    return mfew ? ((mrow >> blk) & 1ull) != 0 : mask_kept(bmrow, blk);
+  };
   auto next_kept = [&](int j) {
     ++j;
     while (j < ntiles && !kept(j)) ++j;
@@ -401,8 +407,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int nqt = (N + BR - 1) / BR;
   const int istart = a.causal ? (k0wg / BR) : 0;
   const int cblk = k0wg / a.mask_block;
+  const bool mfew = a.bmask != nullptr && a.nb <= 64;  // the column's mask fits one 64-bit word
+  const uint64_t mcol = mfew ? mask_bits(a.bmask + cblk, a.nb, a.nb, lane) : ~0ull;
   auto kept = [&](int i) {
-    return a.bmask == nullptr || mask_kept(a.bmask, ((i * BR) / a.mask_block) * a.nb + cblk);
+    if (a.bmask == nullptr) return true;
+    const int blk = (i * BR) / a.mask_block;
+    return mfew ? ((mcol >> blk) & 1ull) != 0 : mask_kept(a.bmask, blk * a.nb + cblk);
   };
   // Query tiles run from the end of the sequence down to the diagonal: every
   // key block of a head then reads the same Q/dO tile at the same iteration,

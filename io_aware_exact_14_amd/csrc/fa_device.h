@@ -263,6 +263,16 @@ __device__ __forceinline__ bool mask_kept(const uint8_t* bm, int idx) {
   return ((*w >> (8u * (uint32_t)(a & 3))) & 0xFFu) != 0;
 }
 
+// Kept bits of up to 64 block-mask bytes at once: lane l (< n) reads the byte
+// at base + l * stride with a vector load; bit l of the wave-uniform result
+// is set when that byte is nonzero. Must be reached by all 64 lanes. With
+// n <= 64 the kernels test these bits instead of walking the mask byte by
+// byte with dependent scalar loads.
+__device__ __forceinline__ uint64_t mask_bits(const uint8_t* base, int stride, int n, int lane) {
+  const uint8_t v = lane < n ? base[(size_t)lane * (size_t)stride] : (uint8_t)0;
+  return __builtin_amdgcn_ballot_w64(v != 0);
+}
+
 // Buffer resource over `bytes` bytes starting at `base` (raw, unstrided).
 // Buffer loads whose per-lane offset falls outside return zeros and such
 // stores are dropped, so tails need no clamping or branches; the

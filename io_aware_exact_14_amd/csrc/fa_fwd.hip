@@ -131,7 +131,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int kend = a.causal ? min(N, qtile0 + C::BR) : N;
   const int ntiles = (kend + BC - 1) / BC;
   const uint8_t* bmrow = a.bmask ? a.bmask + (size_t)(qtile0 / a.mask_block) * a.nb : nullptr;
-  auto kept = [&](int j) { return bmrow == nullptr || mask_kept(bmrow, (j * BC) / a.mask_block); };
+  const bool mfew = bmrow != nullptr && a.nb <= 64;  // the row's mask fits one 64-bit word
+  const uint64_t mrow = mfew ? mask_bits(bmrow, 1, a.nb, lane) : ~0ull;
+  auto kept = [&](int j) {
+    if (bmrow == nullptr) return true;
+    const int blk = (j * BC) / a.mask_block;
+    return mfew ? ((mrow >> blk) & 1ull) != 0 : mask_kept(bmrow, blk);
+  };
   auto next_kept = [&](int j) {
     ++j;
     while (j < ntiles && !kept(j)) ++j;
@@ -507,6 +513,8 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
   const int kend = a.causal ? min(N, q0 + 32) : N;
   const int ntiles = (kend + BC - 1) / BC;
   const uint8_t* bmrow = a.bmask ? a.bmask + (size_t)(q0 / a.mask_block) * a.nb : nullptr;
+  const bool mfew = bmrow != nullptr && a.nb <= 64;
+  const uint64_t mbits = mfew ? mask_bits(bmrow, 1, a.nb, lane) : ~0ull;
 
   T* Ks = reinterpret_cast<T*>(smem) + w * 2 * C::TILE;  // this wave's K tile, then its V tile
   T* Vs = Ks + C::TILE;
@@ -517,7 +525,10 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
   float m_run = NEG_INF, l_run = 0.f;
 
   for (int j = w; j < ntiles; j += 4) {
-    if (bmrow != nullptr && !mask_kept(bmrow, (j * BC) / a.mask_block)) continue;
+    if (bmrow != nullptr) {
+      const int blk = (j * BC) / a.mask_block;
+      if (mfew ? ((mbits >> blk) & 1ull) == 0 : !mask_kept(bmrow, blk)) continue;
+    }
     const int k0 = j * BC;
     // The wave loads its own tile (rows past the end read as zeros). LDS
     // operations of one wave run in order, so these stores follow the reads

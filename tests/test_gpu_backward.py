@@ -176,3 +176,11 @@ def test_side_stream_gives_identical_results(fa):
     torch.cuda.synchronize()
     for a, b in zip((o1, l1) + tuple(g1), (o2, l2) + tuple(g2)):
         assert torch.equal(a, b)
+
+
+def test_block_mask_wider_than_64_blocks(fa):
+    # masks of up to 64 blocks per row are read once into a 64-bit word;
+    # wider ones (here 66 blocks of 128) are walked byte by byte
+    N, mb = 8400, 128
+    bm = random_block_mask((N + mb - 1) // mb, seed=66, frac=0.1)
+    _check_bwd(fa, 1, 1, N, 64, torch.bfloat16, causal=False, bm=bm, mb=mb, in_seed=8400)
