@@ -22,7 +22,8 @@ def _load():
     lib.roofs_valu.argtypes = [ctypes.c_int, ctypes.c_int, d, d, d]
     lib.roofs_lds.argtypes = [ctypes.c_int, d, d, d]
     lib.roofs_copy.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, d, d]
-    for f in (lib.roofs_mfma, lib.roofs_valu, lib.roofs_lds, lib.roofs_copy):
+    lib.roofs_launch.argtypes = [ctypes.c_int, ctypes.c_int, d]
+    for f in (lib.roofs_mfma, lib.roofs_valu, lib.roofs_lds, lib.roofs_copy, lib.roofs_launch):
         f.restype = ctypes.c_int
     return lib
 
@@ -76,9 +77,15 @@ def run_all(cus: int | None = None) -> dict:
             if best is None or r.value > best:
                 best = r.value
     out["hbm_copy_gb_s_best"] = round(best / 1e9, 1)
+    for blocks in (1, 4, 1024):
+        us = _d()
+        if lib.roofs_launch(blocks, 200, ctypes.byref(us)) != 0:
+            raise RuntimeError("roofs_launch failed")
+        out[f"empty_launch_us_{blocks}wg"] = round(us.value, 3)
     out["notes"] = ("MFMA: v_mfma_f32_32x32x16_bf16, 2 waves per SIMD x 4 independent chains, 20000 and 200000 "
                     "iterations. Clocks: s_memtime over s_memrealtime on wave 0 of each kernel. exp/fma: 8 "
                     "independent chains per lane, 4 waves per SIMD. LDS: ds_read_b128, consecutive 16-byte chunks "
                     "per wave, 4 waves per SIMD. HBM: 1 GiB device copy (read + write bytes counted), nontemporal "
-                    "loads and stores, workgroups per CU x 16-byte elements per lane per step swept.")
+                    "loads and stores, workgroups per CU x 16-byte elements per lane per step swept. Launch: 200 "
+                    "back-to-back launches of an empty kernel (1, 4 or 1024 workgroups) between one event pair.")
     return out

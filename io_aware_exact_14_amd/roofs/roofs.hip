@@ -267,4 +267,25 @@ int roofs_copy(int64_t bytes, int blocks_per_cu, int unroll, double* bytes_per_s
   return 0;
 }
 
+// Back-to-back launches of an empty kernel of `blocks` workgroups on one
+// stream, `count` of them between one pair of events: microseconds per launch.
+int roofs_launch(int blocks, int count, double* us_per_launch) {
+  if (blocks <= 0 || count <= 0) return 1;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return 2;
+  for (int i = 0; i < 10; ++i) empty_kernel<<<blocks, 256>>>(nullptr);
+  if (hipDeviceSynchronize() != hipSuccess) return 3;
+  (void)hipEventRecord(e0, nullptr);
+  for (int i = 0; i < count; ++i) empty_kernel<<<blocks, 256>>>(nullptr);
+  (void)hipEventRecord(e1, nullptr);
+  if (hipEventSynchronize(e1) != hipSuccess) return 3;
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (hipGetLastError() != hipSuccess) return 3;
+  *us_per_launch = (double)ms * 1e3 / count;
+  return 0;
+}
+
 }  // extern "C"
