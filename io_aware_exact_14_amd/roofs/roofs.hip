@@ -106,6 +106,11 @@ __global__ void __launch_bounds__(256) lds_kernel(float* out, int iters, unsigne
   out[blockIdx.x * 256 + threadIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
 }
 
+// An empty kernel: the floor of a launch that depends on the previous one.
+__global__ void __launch_bounds__(256) empty_kernel(int* out) {
+  if (out != nullptr && threadIdx.x == 0 && blockIdx.x == 0x7fffffff) out[0] = 0;
+}
+
 // Copy of n 16-byte elements, UNR per lane per step: workgroup g copies the
 // elements g*256*UNR + u*256 + lane over rounds of gridDim.x workgroups.
 template <int UNR>
