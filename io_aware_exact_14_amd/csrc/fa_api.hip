@@ -118,6 +118,7 @@ fa::AttnArgs make_args(const fa_params* p) {
   a.scale = p->scale;
   a.sl2 = (float)((double)p->scale * 1.4426950408889634);
   a.rp = (float)(1.0 / (1.0 - p->dropout_p));
+  a.kq = (float)(1.0 - p->dropout_p);
   a.thresh = (uint32_t)std::floor(p->dropout_p * 65536.0) << 16;
   a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFu);
   a.seed_hi = (uint32_t)(p->seed >> 32);

@@ -123,13 +123,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const float lraw = a.lse[(size_t)bh * N + qc];
   const float lse2 = (!qvalid || lraw == NEG_INF) ? POS_INF : lraw * kLog2e;
   if (qvalid && hi == 0) a.delta[(size_t)bh * N + q] = Dq;
-  // Without dropout the dP products start from -D of this lane's query. The
-  // 16 registers are spent only on the 64-key tiles at d = 64: the 32-key
-  // kernel fits 128 VGPRs without them, which lets four waves share a SIMD.
-  constexpr bool kNegD = !DROP && D == 64 && BC == 64;
+  // The dP products start from -D' of this lane's query, so they yield
+  // dP - D' directly. Without dropout D' = D; the 16 registers are spent
+  // only on the 64-key tiles at d = 64 (the 32-key kernel fits 128 VGPRs
+  // without them, which lets four waves share a SIMD). With dropout the
+  // kernel computes dS' = dS (1 - p) = P * (Z * dP - D (1 - p)), D' =
+  // D (1 - p), and the factor 1 / (1 - p) moves to dQ's final scale.
+  constexpr bool kNegD = (DROP && D == 64) || (D == 64 && BC == 64);
+  const float ndq = DROP ? -Dq * a.kq : -Dq;  // -D'
   f32x16 negd;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) negd[v] = -Dq;
+  for (int v = 0; v < 16; ++v) negd[v] = ndq;
   uint32_t rowhash = 0;
   if constexpr (DROP) {
     const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
@@ -244,27 +248,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             if (kb * 32 + 8 * (v >> 2) + (v & 3) > t) s[kb][v] = NEG_INF;
       }
       const uint32_t y = (rowhash + (uint32_t)(k0 >> 1)) * kMixMul;  // pairs k0/2 + offset: one product per tile
+      const uint32_t t16 = a.thresh >> 16;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float p = exp2_fast(fmaf(s[kb][v], a.sl2, -lse2));
-          float ds = kNegD ? dp[kb][v] : dp[kb][v] - Dq;
-          if constexpr (DROP) {  // dP * Z / (1 - p) - D; elements v, v + 1 (v even) share a keep word
+          float ds = kNegD ? dp[kb][v] : dp[kb][v] + ndq;  // dP - D'
+          if constexpr (DROP) {  // Z * dP - D'; elements v, v + 1 (v even) share a keep word
             const uint32_t off = (uint32_t)(kb * 16 + 4 * (v >> 2) + ((v & 3) >> 1));
             const uint32_t u = keep_finish(y + off * kMixMul);
-            const bool keep = (v & 1) ? keep_hi(u, a.thresh) : keep_lo(u, a.thresh);
-            ds = keep ? fmaf(dp[kb][v], a.rp, -Dq) : -Dq;
+            const bool keep = (v & 1) ? keep_hi(u, a.thresh) : (uint16_t)u >= (uint16_t)t16;
+            ds = keep ? ds : ndq;
           }
-          s[kb][v] = p * ds;  // dS^T
+          s[kb][v] = p * ds;  // dS^T (times 1 - p with dropout)
         }
       if constexpr (KH == 8) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const frag b = pack8<T>(s[kb][8 * hf + 0], s[kb][8 * hf + 1], s[kb][8 * hf + 2], s[kb][8 * hf + 3],
-                                    s[kb][8 * hf + 4], s[kb][8 * hf + 5], s[kb][8 * hf + 6], s[kb][8 * hf + 7]);
+            const frag b = frag4<T>(pack2<T>(s[kb][8 * hf + 0], s[kb][8 * hf + 1]), pack2<T>(s[kb][8 * hf + 2], s[kb][8 * hf + 3]),
+                                    pack2<T>(s[kb][8 * hf + 4], s[kb][8 * hf + 5]), pack2<T>(s[kb][8 * hf + 6], s[kb][8 * hf + 7]));
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
               dq[db] = M::run(S::tr(Ks, kb * 32 + 16 * hf, db * 32, lane), b, dq[db]);
@@ -289,7 +294,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     j = jn;
   }
 
-  const float sc = a.scale;
+  const float sc = DROP ? a.scale * a.rp : a.scale;
   if constexpr (D == 64 && sizeof(T) == 2) {
     // Staged through LDS as in the dK/dV kernel, one 32-column half at a
     // time (four waves' halves fit the tile buffers): each store then writes
@@ -371,14 +376,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int key = k0w + lo;
   const bool kvalid = key < N;
   // Dropout: keys 2m and 2m + 1 (lanes lo and lo ^ 1 of a quad) share the
-  // keep word of pair m. Each lane of the pair computes the words of half of
-  // its 16 queries per block (the even lane elements 0..7, the odd lane
-  // 8..15) and takes the other half from its neighbour by a DPP swap; the
-  // even key reads the low 16 bits, the odd key the high 16.
+  // keep word of pair m; the even key reads its low 16 bits, the odd key its
+  // high 16. For each two adjacent query rows r, r + 1 of a lane, the even
+  // lane computes row r's word and the odd lane row r + 1's; a DPP swap
+  // hands each lane the other word, and one byte permute gathers the lane's
+  // two halves into one dword (row r low, row r + 1 high).
   const uint32_t keyh = (uint32_t)(key >> 1) * kMixMul;  // the row words in LDS are row * kMixMul
   const bool odd = (lo & 1) != 0;
-  const uint32_t hmask = odd ? 0xFFFF0000u : 0x0000FFFFu;
-  const uint32_t hthr = odd ? a.thresh : (a.thresh >> 16);
+  // v_perm_b32(nb, own, sel): bytes 0-3 select own, 4-7 nb.
+  const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
+  const uint32_t t16 = a.thresh >> 16;
 
   // Keys past the end are clamped to row N-1: their scores are masked and
   // their gradients never stored.
@@ -442,7 +449,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const int qic = min(qi, N - 1);
     const float l = Lg[qic];
     l_reg = (qi >= N || l == NEG_INF) ? POS_INF : l * kLog2e;
-    d_reg = -Dg[qic];
+    d_reg = DROP ? -Dg[qic] * a.kq : -Dg[qic];  // -D', D' = D (1 - p) with dropout
     if constexpr (DROP) h_reg = fmix32(hk ^ (uint32_t)qi) * kMixMul;  // row word times the first multiplier
   };
   auto sstore = [&](int buf) {
@@ -456,7 +463,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     if (tid < BR) {
       side_l[buf][tid] = l_reg;
       side_d[buf][tid] = d_reg;
-      side_h[buf][tid] = h_reg;
+      // Rows r0..r3 of each group of four are kept in the order r0 r2 r1 r3:
+      // an even lane reads its words (r0, r2) and an odd lane (r1, r3) as
+      // one 8-byte load.
+      side_h[buf][(tid & ~3) | ((tid & 1) << 1) | ((tid >> 1) & 1)] = h_reg;
     }
   };
 
@@ -528,41 +538,41 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
       for (int qb = 0; qb < NQB; ++qb) {
         bool kbit[16];  // keep bit of element v (dropout only)
         if constexpr (DROP) {
-          uint32_t wown[8];  // words of elements 8 * odd + e
 #pragma unroll
-          for (int gg = 0; gg < 2; ++gg) {
-            const u32x4 h4 = *reinterpret_cast<const u32x4*>(&side_h[cur][qb * 32 + 8 * (gg + 2 * (int)odd) + 4 * hi]);
+          for (int g = 0; g < 4; ++g) {
+            // Elements 4g + 2t, 4g + 2t + 1 are rows r, r + 1 (r = qb*32 + 8g + 4hi + 2t).
+            const u32x2 h2 = *reinterpret_cast<const u32x2*>(&side_h[cur][qb * 32 + 8 * g + 4 * hi + 2 * (int)odd]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wown[4 * gg + e] = keep_finish(h4[e] + keyh);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            // quad_perm [1, 0, 3, 2]: the neighbour's word, elements 8 * (1 - odd) + e
-            const uint32_t wnb = (uint32_t)__builtin_amdgcn_mov_dpp((int)wown[e], 0xB1, 0xF, 0xF, true);
-            const uint32_t wlo = odd ? wnb : wown[e];  // word of element e
-            const uint32_t whi = odd ? wown[e] : wnb;  // word of element e + 8
-            kbit[e] = (wlo & hmask) >= hthr;
-            kbit[e + 8] = (whi & hmask) >= hthr;
+            for (int t = 0; t < 2; ++t) {
+              const uint32_t own = keep_finish(h2[t] + keyh);  // row r + odd
+              // quad_perm [1, 0, 3, 2]: the neighbour's word, row r + 1 - odd
+              const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, true);
+              const uint32_t x = __builtin_amdgcn_perm(nb, own, psel);
+              kbit[4 * g + 2 * t] = (uint16_t)x >= (uint16_t)t16;
+              kbit[4 * g + 2 * t + 1] = x >= a.thresh;
+            }
           }
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int ql = qb * 32 + 8 * g + 4 * hi;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&side_l[cur][ql]);
-          f32x4 nd4 = {0.f, 0.f, 0.f, 0.f};  // -D
+          f32x4 nd4 = {0.f, 0.f, 0.f, 0.f};  // -D'
           if constexpr (DROP) nd4 = *reinterpret_cast<const f32x4*>(&side_d[cur][ql]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int v = 4 * g + e;
             const float p = exp2_fast(fmaf(s[qb][v], a.sl2, -l4[e]));
-            float pd = p, ds = dp[qb][v];  // dP - D
             if constexpr (DROP) {
-              const bool keep = kbit[v];
-              pd = keep ? p : 0.f;                                // 1 / (1 - p) goes on dV at the end
-              ds = keep ? fmaf(dp[qb][v], a.rp, nd4[e]) : nd4[e];  // dP * Z / (1 - p) - D
+              // dS' = P * (Z * dP - D') = P Z dP - P D', D' = D (1 - p); the
+              // factors 1 / (1 - p) go on dK and dV at the end.
+              const float pz = kbit[v] ? p : 0.f;
+              s[qb][v] = pz;
+              dp[qb][v] = fmaf(pz, dp[qb][v], p * nd4[e]);
+            } else {
+              s[qb][v] = p;
+              dp[qb][v] = p * dp[qb][v];  // the products started from -D: dS = P * (dP - D)
             }
-            s[qb][v] = pd;       // P * Z
-            dp[qb][v] = p * ds;  // dS
           }
         }
       }
@@ -571,10 +581,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const frag bp = pack8<T>(s[qb][8 * hf + 0], s[qb][8 * hf + 1], s[qb][8 * hf + 2], s[qb][8 * hf + 3],
-                                     s[qb][8 * hf + 4], s[qb][8 * hf + 5], s[qb][8 * hf + 6], s[qb][8 * hf + 7]);
-            const frag bs = pack8<T>(dp[qb][8 * hf + 0], dp[qb][8 * hf + 1], dp[qb][8 * hf + 2], dp[qb][8 * hf + 3],
-                                     dp[qb][8 * hf + 4], dp[qb][8 * hf + 5], dp[qb][8 * hf + 6], dp[qb][8 * hf + 7]);
+            const frag bp = frag4<T>(pack2<T>(s[qb][8 * hf + 0], s[qb][8 * hf + 1]), pack2<T>(s[qb][8 * hf + 2], s[qb][8 * hf + 3]),
+                                     pack2<T>(s[qb][8 * hf + 4], s[qb][8 * hf + 5]), pack2<T>(s[qb][8 * hf + 6], s[qb][8 * hf + 7]));
+            const frag bs = frag4<T>(pack2<T>(dp[qb][8 * hf + 0], dp[qb][8 * hf + 1]), pack2<T>(dp[qb][8 * hf + 2], dp[qb][8 * hf + 3]),
+                                     pack2<T>(dp[qb][8 * hf + 4], dp[qb][8 * hf + 5]), pack2<T>(dp[qb][8 * hf + 6], dp[qb][8 * hf + 7]));
             const int base = qb * 32 + 16 * hf;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
@@ -602,8 +612,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     it = itn;
   }
 
-  const float sc = a.scale;
-  const float sv = DROP ? a.rp : 1.f;  // dV = sum_i (P * Z)_ij dO_i / (1 - p)
+  const float sc = DROP ? a.scale * a.rp : a.scale;  // dK = scale * sum_i dS'_ij Q_i / (1 - p)
+  const float sv = DROP ? a.rp : 1.f;                // dV = sum_i (P * Z)_ij dO_i / (1 - p)
   if constexpr (D == 64 && sizeof(T) == 2) {
     // A lane holds 4-value pieces of 32 rows, so a direct store writes 32
     // bytes to each of 32 rows. Each wave instead stages its 32 rows in LDS

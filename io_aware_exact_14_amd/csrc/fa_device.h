@@ -104,6 +104,38 @@ __device__ __forceinline__ typename Mfma<T>::frag pack8(float x0, float x1, floa
 
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 
+// Two fp32 values -> one dword holding them as 16-bit values (round to
+// nearest even), x0 in the low half. Converting the pair as a two-element
+// vector gives one packed conversion instruction.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ uint32_t pack2(float x0, float x1);
+template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+}
+template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, f16x2));
+}
+
+// acc + both 16-bit values of a packed dword: a two-term dot product with
+// (1, 1), so a row sum over packed values costs one instruction per pair.
+template <typename T> __device__ __forceinline__ float add_pair(uint32_t pk, float acc);
+template <> __device__ __forceinline__ float add_pair<__bf16>(uint32_t pk, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+}
+template <> __device__ __forceinline__ float add_pair<_Float16>(uint32_t pk, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
+}
+
+// Four packed dwords (elements 2e, 2e + 1 in dword e) -> one fragment.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag frag4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+  return __builtin_bit_cast(typename Mfma<T>::frag, u32x4{d0, d1, d2, d3});
+}
+
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -154,6 +186,11 @@ __device__ __forceinline__ u16x2 keep01(uint32_t u, u16x2 tm1, u16x2 ones) {
   return __builtin_elementwise_min(__builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, u), tm1), ones);
 }
 __device__ __forceinline__ bool keep_lo(uint32_t u, uint32_t thresh) { return (u << 16) >= thresh; }
+// A packed pair of 16-bit P values (low half: the even key) with the pair's
+// keep word u applied.
+__device__ __forceinline__ uint32_t keep_pair(uint32_t pk, uint32_t u, u16x2 tm1, u16x2 ones) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, pk) * keep01(u, tm1, ones));
+}
 
 // Per-(b, h) dropout key from the 64-bit seed.
 __device__ __forceinline__ uint32_t head_key(uint32_t seed_lo, uint32_t seed_hi, uint32_t b, uint32_t h) {

@@ -229,6 +229,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const bool active = (q0b[0] < N) && (!a.causal || k0 <= qlast);
     if (active) {
       f32x16 s[QB][NKB];
+      uint32_t pk[QB][NKB][8];  // 16-bit operand types: P as packed pairs
 #pragma unroll
       for (int b = 0; b < QB; ++b)
 #pragma unroll
@@ -283,16 +284,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             for (int v = 0; v < 16; ++v) o[b][db][v] *= alpha;
         }
         const float base = (m_run[b] == NEG_INF) ? 0.f : m_run[b];
-        float rs = 0.f;
+        if constexpr (KH == 8) {
+          // P goes straight to packed 16-bit pairs (the MFMA operand); the
+          // row sum adds those pairs, so it sums the values the MFMA uses.
+          float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+          for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float p = exp2_fast(fmaf(s[b][kb][v], a.sl2, -base));
-            rs += p;
-            s[b][kb][v] = p;
-          }
-        l_run[b] += rs;
+            for (int e = 0; e < 8; ++e) {
+              const float p0 = exp2_fast(fmaf(s[b][kb][2 * e], a.sl2, -base));
+              const float p1 = exp2_fast(fmaf(s[b][kb][2 * e + 1], a.sl2, -base));
+              pk[b][kb][e] = pack2<T>(p0, p1);
+              if (e & 1)
+                rs1 = add_pair<T>(pk[b][kb][e], rs1);
+              else
+                rs0 = add_pair<T>(pk[b][kb][e], rs0);
+            }
+          l_run[b] += rs0 + rs1;
+        } else {
+          float rs = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float p = exp2_fast(fmaf(s[b][kb][v], a.sl2, -base));
+              rs += p;
+              s[b][kb][v] = p;
+            }
+          l_run[b] += rs;
+        }
 
         if constexpr (DROP && KH != 8) {
           // Keys k0 + kb*32 + crow(v, hi); elements v and v + 1 (v even) are
@@ -334,19 +354,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             frag pb[QB];
 #pragma unroll
             for (int b = 0; b < QB; ++b) {
-              pb[b] = pack8<T>(s[b][kb][8 * hf + 0], s[b][kb][8 * hf + 1], s[b][kb][8 * hf + 2], s[b][kb][8 * hf + 3],
-                               s[b][kb][8 * hf + 4], s[b][kb][8 * hf + 5], s[b][kb][8 * hf + 6], s[b][kb][8 * hf + 7]);
-              if constexpr (DROP) {
-                u16x8 km;
+              uint32_t d4[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+              for (int e = 0; e < 4; ++e) {
+                d4[e] = pk[b][kb][4 * hf + e];
+                if constexpr (DROP) {
                   const uint32_t off = (uint32_t)(kb * 16 + 8 * hf + 4 * (e >> 1) + (e & 1));
-                  const u16x2 k2 = keep01(keep_finish(ytile[b] + off * kMixMul), tm1, ones);
-                  km[2 * e] = k2[0];
-                  km[2 * e + 1] = k2[1];
+                  d4[e] = keep_pair(d4[e], keep_finish(ytile[b] + off * kMixMul), tm1, ones);
                 }
-                pb[b] = __builtin_bit_cast(frag, __builtin_bit_cast(u16x8, pb[b]) * km);
               }
+              pb[b] = frag4<T>(d4[0], d4[1], d4[2], d4[3]);
             }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
@@ -577,11 +594,20 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
     }
     const float base = (m_run == NEG_INF) ? 0.f : m_run;
+    uint32_t pk[8];  // 16-bit operand types: P as packed pairs, summed as such
+    if constexpr (KH == 8) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float pv = exp2_fast(fmaf(sc[v], a.sl2, -base));
-      l_run += pv;
-      sc[v] = pv;
+      for (int e = 0; e < 8; ++e) {
+        pk[e] = pack2<T>(exp2_fast(fmaf(sc[2 * e], a.sl2, -base)), exp2_fast(fmaf(sc[2 * e + 1], a.sl2, -base)));
+        l_run = add_pair<T>(pk[e], l_run);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = exp2_fast(fmaf(sc[v], a.sl2, -base));
+        l_run += pv;
+        sc[v] = pv;
+      }
     }
     const uint32_t y = DROP ? (rowhash + (uint32_t)(k0 >> 1)) * kMixMul : 0u;
     if constexpr (DROP && KH != 8) {
@@ -597,18 +623,14 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
       const u16x2 ones = __builtin_bit_cast(u16x2, a.ones16);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        frag pb = pack8<T>(sc[8 * hf + 0], sc[8 * hf + 1], sc[8 * hf + 2], sc[8 * hf + 3], sc[8 * hf + 4],
-                           sc[8 * hf + 5], sc[8 * hf + 6], sc[8 * hf + 7]);
-        if constexpr (DROP) {  // packed keep factors, as in the 128-row kernel (T16 >= 1)
-          u16x8 km;
+        uint32_t d4[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const u16x2 k2 = keep01(keep_finish(y + (uint32_t)(8 * hf + 4 * (e >> 1) + (e & 1)) * kMixMul), tm1, ones);
-            km[2 * e] = k2[0];
-            km[2 * e + 1] = k2[1];
-          }
-          pb = __builtin_bit_cast(frag, __builtin_bit_cast(u16x8, pb) * km);
+        for (int e = 0; e < 4; ++e) {
+          d4[e] = pk[4 * hf + e];
+          if constexpr (DROP)  // packed keep factors, as in the 128-row kernel (T16 >= 1)
+            d4[e] = keep_pair(d4[e], keep_finish(y + (uint32_t)(8 * hf + 4 * (e >> 1) + (e & 1)) * kMixMul), tm1, ones);
         }
+        const frag pb = frag4<T>(d4[0], d4[1], d4[2], d4[3]);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] = M::run(load_frag_tr_rp<T>(Vs, C::KS, 16 * hf, db * 32, lane), pb, o[db]);
       }

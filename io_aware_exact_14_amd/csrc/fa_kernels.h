@@ -33,6 +33,7 @@ struct AttnArgs {
   float scale;       // softmax scale
   float sl2;         // scale * log2(e)
   float rp;          // 1 / (1 - dropout_p)
+  float kq;          // 1 - dropout_p
   uint32_t thresh;   // dropout threshold floor(p * 2^16) << 16: a key is kept when its
                      // 16-bit half of the keep word, moved to the top bits, is >= thresh
   uint32_t seed_lo;
