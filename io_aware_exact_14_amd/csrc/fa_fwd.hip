@@ -700,7 +700,7 @@ template <typename T, int D, int BC, int QB, bool DROP>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
   const int nq = (a.N + 128 * QB - 1) / (128 * QB);
   const dim3 grid((unsigned)(nq * a.BH));
-  constexpr int WPE = D * QB > 128 ? 1 : (D == 64 && !DROP && sizeof(T) == 2 ? 4 : 2);  // two query blocks at d = 128 need the whole register file
+  constexpr int WPE = D * QB > 128 ? 1 : (D == 64 && sizeof(T) == 2 ? 4 : 2);  // two query blocks at d = 128 need the whole register file
   fwd_kernel<T, D, BC, QB, DROP, WPE><<<grid, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
