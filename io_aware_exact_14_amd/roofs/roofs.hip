@@ -1,6 +1,7 @@
 // Microbenchmarks of the MI355X roofs that the attention kernels are measured
-// against: bf16 MFMA rate and the shader clock it runs at, v_exp_f32 and
-// fp32 FMA issue rates, LDS read bandwidth, and an HBM copy. Each entry point
+// against: bf16 MFMA rate and the shader clock it runs at, issue rates of the
+// VALU instructions the kernels use, MFMA / VALU overlap, LDS read bandwidth
+// (plain and transpose reads), an HBM copy and the empty-launch floor. Each entry point
 // runs one timed launch (after one warm-up launch) on the current device and
 // returns its results through pointers; every loop has a fixed trip count and
 // every access stays inside the buffers the entry point allocates.
@@ -56,32 +57,81 @@ __global__ void __launch_bounds__(256) mfma_kernel(float* out, int iters, unsign
   stamp_store(stamps, s0, s1);
 }
 
-// Eight independent chains x = exp2(-x) (stays in (0, 1]) per lane.
-__global__ void __launch_bounds__(256) exp_kernel(float* out, int iters, unsigned long long* stamps) {
+// Issue rate of one VALU instruction kind: eight independent chains per lane
+// of that instruction (kinds below), 4 waves per SIMD. The chains keep their
+// values bounded and every result is consumed, so nothing is folded away.
+//   0 v_exp_f32            x = exp2(-x)
+//   1 v_fma_f32            x = x * a + b (a < 1)
+//   2 v_dot2c_f32_bf16     x += dot((bf16 pair), (1, 1))
+//   3 v_mul_lo_u32         u = u * c
+//   4 v_perm_b32           u = perm(u, c, selector)
+//   5 v_cvt_pk_bf16_f32    u = bits of the bf16 pair (u as float, a)
+//   6 v_pk_mul_lo_u16      u = u * c, two 16-bit halves
+//   7 v_cmp + v_cndmask    x = x > a ? x : a + 0.5 (two instructions per step)
+//   8 v_mov_b32_dpp + add  u = quad_perm[1,0,3,2](u) + c (two instructions per step)
+//   9 exp and fma mixed    chains 0-3 as kind 0, chains 4-7 as kind 1
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+template <int KIND>
+__global__ void __launch_bounds__(256) rate_kernel(float* out, int iters, float a, uint32_t c, unsigned long long* stamps) {
   float x[8];
-  for (int k = 0; k < 8; ++k) x[k] = 0.01f * (float)(threadIdx.x + k);
+  uint32_t u[8];
+  for (int k = 0; k < 8; ++k) {
+    x[k] = 0.01f * (float)(threadIdx.x + k);
+    u[k] = threadIdx.x * 2654435761u + (uint32_t)k;
+  }
   const Stamp s0 = stamp_now();
   for (int i = 0; i < iters; ++i)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = __builtin_amdgcn_exp2f(-x[k]);
+    for (int k = 0; k < 8; ++k) {
+      if constexpr (KIND == 0) x[k] = __builtin_amdgcn_exp2f(-x[k]);
+      if constexpr (KIND == 1) x[k] = __builtin_fmaf(x[k], a, 0.001f);
+      if constexpr (KIND == 2)
+        x[k] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u[k]), __builtin_bit_cast(bf16x2, c), x[k], false);
+      if constexpr (KIND == 3) u[k] = u[k] * c;
+      if constexpr (KIND == 4) u[k] = __builtin_amdgcn_perm(u[k], c, 0x05040100u + (uint32_t)k);
+      if constexpr (KIND == 5)
+        u[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{__builtin_bit_cast(float, u[k]), a}, bf16x2));
+      if constexpr (KIND == 6) u[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, u[k]) * __builtin_bit_cast(u16x2, c));
+      if constexpr (KIND == 7) x[k] = x[k] > a ? x[k] : a + 0.5f;
+      if constexpr (KIND == 8) u[k] = (uint32_t)__builtin_amdgcn_mov_dpp((int)u[k], 0xB1, 0xF, 0xF, true) + c;
+      if constexpr (KIND == 9) {
+        if (k < 4)
+          x[k] = __builtin_amdgcn_exp2f(-x[k]);
+        else
+          x[k] = __builtin_fmaf(x[k], a, 0.001f);
+      }
+    }
   stamp_store(stamps, s0, stamp_now());
   float s = 0.f;
-  for (int k = 0; k < 8; ++k) s += x[k];
+  for (int k = 0; k < 8; ++k) s += x[k] + (float)(u[k] & 7u);
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-// Eight independent chains x = x * a + b (a < 1 keeps them bounded) per lane.
-__global__ void __launch_bounds__(256) fma_kernel(float* out, int iters, float a, float b,
-                                                  unsigned long long* stamps) {
+// MFMA / VALU overlap: per iteration two independent v_mfma_f32_32x32x16_bf16
+// (64 cycles of the matrix pipe) and NV fp32 FMAs on other registers.
+template <int NV>
+__global__ void __launch_bounds__(256) overlap_kernel(float* out, int iters, float a, unsigned long long* stamps) {
+  bf16x8 p, q;
+  for (int i = 0; i < 8; ++i) {
+    p[i] = (__bf16)(0.001f * (float)(threadIdx.x + i));
+    q[i] = (__bf16)(0.002f * (float)(i - 3));
+  }
+  f32x16 c0 = {}, c1 = {};
   float x[8];
   for (int k = 0; k < 8; ++k) x[k] = 0.01f * (float)(threadIdx.x + k);
   const Stamp s0 = stamp_now();
-  for (int i = 0; i < iters; ++i)
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p, q, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q, p, c1, 0, 0, 0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = __builtin_fmaf(x[k], a, b);
+    for (int r = 0; r < NV; ++r) x[r & 7] = __builtin_fmaf(x[r & 7], a, 0.001f);
+  }
   stamp_store(stamps, s0, stamp_now());
   float s = 0.f;
   for (int k = 0; k < 8; ++k) s += x[k];
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i];
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
@@ -104,6 +154,37 @@ __global__ void __launch_bounds__(256) lds_kernel(float* out, int iters, unsigne
   }
   stamp_store(stamps, s0, stamp_now());
   out[blockIdx.x * 256 + threadIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
+}
+
+// Transpose reads in the pattern of the attention kernels' V^T / K^T
+// operands: a 64-row bf16 tile with rows padded to 72 elements; per step each
+// lane issues two ds_read_b64_tr_b16 (rows 4*(j/4) + l/32 and 2 further,
+// 16-element column group (l/16)&1, 4-element piece j&3 for j = l&15), i.e.
+// 16 bytes per lane like the ds_read_b128 kernel.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__global__ void __launch_bounds__(256) lds_tr_kernel(float* out, int iters, unsigned long long* stamps) {
+  constexpr int KS = 72;
+  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * KS];
+  for (int i = threadIdx.x; i < 64 * KS; i += 256) tile[i] = (__bf16)(float)(i & 255);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  uint32_t a0 = 0, a1 = 0;
+  const Stamp s0 = stamp_now();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int base = 16 * (k & 3), col0 = 32 * (k >> 2);  // rows base..base+15, columns col0..col0+31
+      const __bf16* pp = tile + (base + 4 * (j >> 2) + (lane >> 5)) * KS + col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      const u32x2_t x = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pp));
+      const u32x2_t y = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pp + 2 * KS)));
+      a0 ^= x[0] ^ y[0];  // two-input XORs fold into v_xor3_b32
+      a1 ^= x[1] ^ y[1];
+    }
+  }
+  stamp_store(stamps, s0, stamp_now());
+  out[blockIdx.x * 256 + threadIdx.x] = (float)(a0 + a1);
 }
 
 // An empty kernel: the floor of a launch that depends on the previous one.
@@ -195,18 +276,33 @@ int roofs_mfma(int iters, int waves_per_simd, double* tflops, double* clock_ghz,
   return 0;
 }
 
-// v_exp_f32 (kind 0) or fp32 FMA (kind 1): wave-level instructions per second
-// with 4 waves per SIMD, and the clock they ran at.
+// Instruction kind `kind` of rate_kernel (0-9): wave-level loop steps per
+// second (kinds 7 and 8 issue two instructions per step) with 4 waves per
+// SIMD, and the clock they ran at.
 int roofs_valu(int kind, int iters, double* winst_per_s, double* clock_ghz, double* ms_out) {
   const int cus = device_cus();
-  if (cus <= 0 || iters <= 0) return 1;
+  if (cus <= 0 || iters <= 0 || kind < 0 || kind > 9) return 1;
   const int blocks = cus * 4;
   float* out = nullptr;
   unsigned long long* st = nullptr;
   if (hipMalloc(&out, (size_t)blocks * 256 * sizeof(float)) != hipSuccess) return 2;
   if (hipMalloc(&st, 2 * sizeof(unsigned long long)) != hipSuccess) return 2;
-  const double ms = kind == 0 ? timed([&] { exp_kernel<<<blocks, 256>>>(out, iters, st); })
-                              : timed([&] { fma_kernel<<<blocks, 256>>>(out, iters, 0.999f, 0.001f, st); });
+  const float a = 0.999f;
+  const uint32_t c = 0x3F803F80u;  // (1, 1) in bf16; an odd multiplier for the integer kinds
+  const double ms = timed([&] {
+    switch (kind) {
+      case 0: rate_kernel<0><<<blocks, 256>>>(out, iters, a, c, st); break;
+      case 1: rate_kernel<1><<<blocks, 256>>>(out, iters, a, c, st); break;
+      case 2: rate_kernel<2><<<blocks, 256>>>(out, iters, a, c, st); break;
+      case 3: rate_kernel<3><<<blocks, 256>>>(out, iters, a, c, st); break;
+      case 4: rate_kernel<4><<<blocks, 256>>>(out, iters, a, c, st); break;
+      case 5: rate_kernel<5><<<blocks, 256>>>(out, iters, a, c, st); break;
+      case 6: rate_kernel<6><<<blocks, 256>>>(out, iters, a, c, st); break;
+      case 7: rate_kernel<7><<<blocks, 256>>>(out, iters, a, c, st); break;
+      case 8: rate_kernel<8><<<blocks, 256>>>(out, iters, a, c, st); break;
+      default: rate_kernel<9><<<blocks, 256>>>(out, iters, a, c, st); break;
+    }
+  });
   *clock_ghz = stamp_ghz(st);
   (void)hipFree(out);
   (void)hipFree(st);
@@ -216,9 +312,10 @@ int roofs_valu(int kind, int iters, double* winst_per_s, double* clock_ghz, doub
   return 0;
 }
 
-// ds_read_b128 bytes per second over the whole device (4 waves per SIMD),
-// and the clock.
-int roofs_lds(int iters, double* bytes_per_s, double* clock_ghz, double* ms_out) {
+// overlap_kernel with nv (0, 4, 8, 12, 16 or 24) FMAs per two MFMAs:
+// shader cycles per SIMD per iteration of one wave (4 waves per SIMD), and
+// the clock.
+int roofs_overlap(int nv, int iters, double* cycles, double* clock_ghz) {
   const int cus = device_cus();
   if (cus <= 0 || iters <= 0) return 1;
   const int blocks = cus * 4;
@@ -226,7 +323,38 @@ int roofs_lds(int iters, double* bytes_per_s, double* clock_ghz, double* ms_out)
   unsigned long long* st = nullptr;
   if (hipMalloc(&out, (size_t)blocks * 256 * sizeof(float)) != hipSuccess) return 2;
   if (hipMalloc(&st, 2 * sizeof(unsigned long long)) != hipSuccess) return 2;
-  const double ms = timed([&] { lds_kernel<<<blocks, 256>>>(out, iters, st); });
+  const double ms = timed([&] {
+    switch (nv) {
+      case 0: overlap_kernel<0><<<blocks, 256>>>(out, iters, 0.999f, st); break;
+      case 4: overlap_kernel<4><<<blocks, 256>>>(out, iters, 0.999f, st); break;
+      case 8: overlap_kernel<8><<<blocks, 256>>>(out, iters, 0.999f, st); break;
+      case 12: overlap_kernel<12><<<blocks, 256>>>(out, iters, 0.999f, st); break;
+      case 16: overlap_kernel<16><<<blocks, 256>>>(out, iters, 0.999f, st); break;
+      case 24: overlap_kernel<24><<<blocks, 256>>>(out, iters, 0.999f, st); break;
+      default: break;
+    }
+  });
+  *clock_ghz = stamp_ghz(st);
+  (void)hipFree(out);
+  (void)hipFree(st);
+  if (ms <= 0.0) return 3;
+  *cycles = *clock_ghz * 1e9 * ms * 1e-3 / (4.0 * iters);
+  return 0;
+}
+
+// LDS read bytes per second over the whole device (4 waves per SIMD), and
+// the clock: kind 0 ds_read_b128 of consecutive chunks, kind 1 the
+// transpose-read pattern of lds_tr_kernel.
+int roofs_lds(int kind, int iters, double* bytes_per_s, double* clock_ghz, double* ms_out) {
+  const int cus = device_cus();
+  if (cus <= 0 || iters <= 0 || kind < 0 || kind > 1) return 1;
+  const int blocks = cus * 4;
+  float* out = nullptr;
+  unsigned long long* st = nullptr;
+  if (hipMalloc(&out, (size_t)blocks * 256 * sizeof(float)) != hipSuccess) return 2;
+  if (hipMalloc(&st, 2 * sizeof(unsigned long long)) != hipSuccess) return 2;
+  const double ms = kind == 0 ? timed([&] { lds_kernel<<<blocks, 256>>>(out, iters, st); })
+                              : timed([&] { lds_tr_kernel<<<blocks, 256>>>(out, iters, st); });
   *clock_ghz = stamp_ghz(st);
   (void)hipFree(out);
   (void)hipFree(st);
