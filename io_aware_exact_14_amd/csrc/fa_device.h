@@ -90,18 +90,6 @@ __device__ __forceinline__ typename Mfma<T>::frag load_frag_2x4(const T* p0, con
 
 template <typename T> __device__ __forceinline__ T from_f32(float x) { return static_cast<T>(x); }
 
-// Eight fp32 values -> one 16-bit fragment (round to nearest even).
-template <typename T>
-__device__ __forceinline__ typename Mfma<T>::frag pack8(float x0, float x1, float x2, float x3,
-                                                          float x4, float x5, float x6, float x7) {
-  typename Mfma<T>::frag f;
-  f[0] = static_cast<T>(x0); f[1] = static_cast<T>(x1);
-  f[2] = static_cast<T>(x2); f[3] = static_cast<T>(x3);
-  f[4] = static_cast<T>(x4); f[5] = static_cast<T>(x5);
-  f[6] = static_cast<T>(x6); f[7] = static_cast<T>(x7);
-  return f;
-}
-
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 
 // Two fp32 values -> one dword holding them as 16-bit values (round to
@@ -118,24 +106,11 @@ template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float x0, float 
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, f16x2));
 }
 
-// acc + both 16-bit values of a packed dword: a two-term dot product with
-// (1, 1), so a row sum over packed values costs one instruction per pair.
-template <typename T> __device__ __forceinline__ float add_pair(uint32_t pk, float acc);
-template <> __device__ __forceinline__ float add_pair<__bf16>(uint32_t pk, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
-}
-template <> __device__ __forceinline__ float add_pair<_Float16>(uint32_t pk, float acc) {
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
-}
-
 // Four packed dwords (elements 2e, 2e + 1 in dword e) -> one fragment.
 template <typename T>
 __device__ __forceinline__ typename Mfma<T>::frag frag4(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
   return __builtin_bit_cast(typename Mfma<T>::frag, u32x4{d0, d1, d2, d3});
 }
-
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -179,7 +154,6 @@ __device__ __forceinline__ bool keep_hi(uint32_t u, uint32_t thresh) { return u 
 // (tm1 = T16 - 1 in both halves; T16 >= 1). Multiplying the bits of a
 // packed 16-bit pair of P by it keeps or zeroes each value exactly.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 // `ones` is {1, 1} passed at run time (AttnArgs::ones16): with a literal 1
 // the compiler rewrites the min into two compares and selects.
 __device__ __forceinline__ u16x2 keep01(uint32_t u, u16x2 tm1, u16x2 ones) {

@@ -286,8 +286,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         const float base = (m_run[b] == NEG_INF) ? 0.f : m_run[b];
         if constexpr (KH == 8) {
           // P goes straight to packed 16-bit pairs (the MFMA operand); the
-          // row sum adds those pairs, so it sums the values the MFMA uses.
-          float rs0 = 0.f, rs1 = 0.f;
+          // row sum adds the fp32 values, so LSE keeps fp32 accuracy.
+          float rs = 0.f;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -295,12 +295,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
               const float p0 = exp2_fast(fmaf(s[b][kb][2 * e], a.sl2, -base));
               const float p1 = exp2_fast(fmaf(s[b][kb][2 * e + 1], a.sl2, -base));
               pk[b][kb][e] = pack2<T>(p0, p1);
-              if (e & 1)
-                rs1 = add_pair<T>(pk[b][kb][e], rs1);
-              else
-                rs0 = add_pair<T>(pk[b][kb][e], rs0);
+              rs += p0 + p1;
             }
-          l_run[b] += rs0 + rs1;
+          l_run[b] += rs;
         } else {
           float rs = 0.f;
 #pragma unroll
@@ -594,12 +591,14 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
     }
     const float base = (m_run == NEG_INF) ? 0.f : m_run;
-    uint32_t pk[8];  // 16-bit operand types: P as packed pairs, summed as such
+    uint32_t pk[8];  // 16-bit operand types: P as packed pairs
     if constexpr (KH == 8) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pk[e] = pack2<T>(exp2_fast(fmaf(sc[2 * e], a.sl2, -base)), exp2_fast(fmaf(sc[2 * e + 1], a.sl2, -base)));
-        l_run = add_pair<T>(pk[e], l_run);
+        const float p0 = exp2_fast(fmaf(sc[2 * e], a.sl2, -base));
+        const float p1 = exp2_fast(fmaf(sc[2 * e + 1], a.sl2, -base));
+        pk[e] = pack2<T>(p0, p1);
+        l_run += p0 + p1;
       }
     } else {
 #pragma unroll
