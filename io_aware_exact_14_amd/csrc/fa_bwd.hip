@@ -7,6 +7,9 @@
 // forward definition, with Pd = P * Z / (1 - p):
 //   dV = Pd^T dO,  dP = (dO V^T) * Z / (1 - p),  D_i = dO_i . O_i,
 //   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+// With dropout the kernels form dS' = dS (1 - p) = P * (Z * (dO V^T) - D (1 - p))
+// and fold 1 / (1 - p) into the final scales of dQ and dK (dV's factor is
+// applied at the end too), which saves a multiply per score.
 //
 // Two kernels, both deterministic (no atomics):
 //   bwd_dq_kernel   one workgroup per 128 query rows: D_i (written to the
@@ -353,8 +356,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 
   __shared__ __attribute__((aligned(16))) T smem[2][2 * TILE];  // [buffer][Q tile | dO tile]
   __shared__ __attribute__((aligned(16))) float side_l[2][BR];  // LSE in log2 units (+inf: no valid key)
-  __shared__ __attribute__((aligned(16))) float side_d[2][BR];  // -D_i
-  __shared__ __attribute__((aligned(16))) uint32_t side_h[2][BR];  // dropout row hash
+  __shared__ __attribute__((aligned(16))) float side_d[2][BR];  // -D_i (times 1 - p with dropout)
+  __shared__ __attribute__((aligned(16))) uint32_t side_h[2][BR];  // dropout row words, in the order r0 r2 r1 r3 per four rows
   __shared__ __attribute__((aligned(16))) T vsm[VLDS ? BK * S::KS : 8];  // V rows of this workgroup
 
   const int tid = threadIdx.x;
