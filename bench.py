@@ -240,13 +240,26 @@ def _tiled_step_fn(lib, p, q, k, v, do, o, lse, dq, dk, dv, ws, stream):
     return fwd, bwd
 
 
-def _time_fwd_bwd(fwd, bwd, steps, warmup, stream):
-    """(ms per fwd+bwd step by wall clock, forward ms, backward ms by HIP events)."""
+def _time_fwd_bwd(fwd, bwd, steps, warmup, stream, warm_ms=0.0):
+    """(ms per fwd+bwd step by wall clock, forward ms, backward ms by HIP events).
+    With ``warm_ms`` > 0, untimed steps run for about that much device time
+    after the warm-up steps (the clock ramps up under sustained load)."""
     import torch
 
     for _ in range(warmup):
         fwd()
         bwd()
+    if warm_ms > 0.0:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fwd()
+        bwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        one = max(e0.elapsed_time(e1), 1e-3)
+        for _ in range(int(math.ceil(warm_ms / one))):
+            fwd()
+            bwd()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -415,7 +428,7 @@ def run_sweep(args):
                              device=dev)
             t_fwd, t_bwd = _tiled_step_fn(lib, p, q, k, v, do, o, lse, dq, dk, dv, ws, stream)
             steps = max(3, min(args.steps, int(2e5 // N)))
-            ms, fm, bm = _time_fwd_bwd(t_fwd, t_bwd, steps, max(1, min(args.warmup, 3)), stream)
+            ms, fm, bm = _time_fwd_bwd(t_fwd, t_bwd, steps, max(1, min(args.warmup, 3)), stream, args.warm_ms)
             fwd_fl = 4.0 * B * H * N * N * d * 0.5
             del o, lse, dq, dk, dv, ws
             row = {"N": N, "B": B, "H": H, "d": d, "steps": steps,
