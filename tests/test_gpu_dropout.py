@@ -69,7 +69,8 @@ def test_keep_bits_used_inside_forward(fa, p, dtype):
 
 @pytest.mark.parametrize("N", [1024, 4096, 4608])
 @pytest.mark.parametrize("p", [0.1, 0.37])
-def test_keep_bits_inside_d64_kernels(fa, N, p):
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_keep_bits_inside_d64_kernels(fa, N, p, dtype):
     # The d = 64 launch configurations (the dropout workload's: forward with
     # 64-key tiles, dQ with 32-key tiles up to 4096 keys and 64-key tiles
     # beyond, dK/dV with 32-row tiles up to 2048 keys and 64-row tiles beyond)
@@ -87,7 +88,7 @@ def test_keep_bits_inside_d64_kernels(fa, N, p):
     perm = np.random.default_rng(N).permutation(nb)
     bm = np.zeros((nb, nb), np.uint8)
     bm[np.arange(nb), perm] = 1
-    B, H, seed, dtype = 1, 2, 0xA5A5F00D0123, torch.bfloat16
+    B, H, seed = 1, 2, 0xA5A5F00D0123
     scale = 1.0 / math.sqrt(d)
     ar = torch.arange(N)
     lvl = torch.where(ar % 128 < 64, 1.0, 2.0)
@@ -99,7 +100,7 @@ def test_keep_bits_inside_d64_kernels(fa, N, p):
     e0[:, :, :, 0] = 1
     ones = torch.ones(B, H, N, d, dtype=dtype)
     kw = dict(scale=scale, dropout_p=p, seed=seed, block_mask=torch.from_numpy(bm), mask_block=mb)
-    note(f"dropout probe d=64 N={N} p={p}")
+    note(f"dropout probe d=64 N={N} p={p} {dtype}")
     krand = torch.randn(B, H, N, d).to(dtype)
     # forward and dK/dV: K arbitrary (Q = 0 ignores it), V = X, dO = X
     qd, kd, vd = to_dev(q, krand, X)
