@@ -64,9 +64,12 @@ constexpr float kLazyRescale = 8.0f;
 
 // QB: 32-query blocks per wave. Every K fragment and every V^T transpose read
 // taken from LDS feeds QB MFMAs, which divides the LDS read traffic per
-// flop by QB (LDS bandwidth, not MFMA, bounds a wave with a single block).
-// Wave w owns the query blocks w, w + 4, ... of the workgroup tile, so causal
-// work is spread evenly over the waves.
+// flop by QB. Wave w owns the query blocks w, w + 4, ... of the workgroup
+// tile, so causal work is spread evenly over the waves. The launches use
+// QB = 1 (QB = 2 measured slower at every workload: the register file then
+// holds two waves per SIMD); a workgroup of QB > 1 spans 128 * QB rows but
+// reads the block-mask row of its first 128, so the host refuses QB > 1 with
+// a block mask.
 template <typename T, int D, int BC, int QB, bool DROP, int WPE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) fwd_kernel(AttnArgs a) {
   using C = FwdCfg<T, D, BC, QB>;
@@ -693,8 +696,8 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
 // Resident waves per SIMD: with one wave, softmax VALU work, LDS reads and
 // MFMAs of a tile run back to back; more waves let them overlap. d = 128
 // fits two waves (256 VGPRs, two workgroups' LDS in the 160 KB of a CU);
-// the 16-bit d = 64 kernel without dropout is held to 128 VGPRs for four
-// (a 16-byte spill, cheaper than the lost occupancy).
+// the 16-bit d = 64 kernel, with or without dropout, fits 128 VGPRs for
+// four (with P packed pairwise the dropout variant needs no spill).
 template <typename T, int D, int BC, int QB, bool DROP>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
   const int nq = (a.N + 128 * QB - 1) / (128 * QB);
@@ -719,6 +722,7 @@ static hipError_t launch_fwd_split(bool dropout, const AttnArgs& a, hipStream_t 
 
 template <typename T, int D, int BC, int QB>
 static hipError_t launch_fwd_d(bool dropout, const AttnArgs& a, hipStream_t s) {
+  if (QB > 1 && a.bmask != nullptr) return hipErrorInvalidValue;
   const long tiles = (long)((a.N + 127) / 128) * a.BH;
   if (4 * tiles <= a.ncu) return launch_fwd_split<T, D>(dropout, a, s);
   return dropout ? launch_fwd_t<T, D, BC, QB, true>(a, s) : launch_fwd_t<T, D, BC, QB, false>(a, s);
