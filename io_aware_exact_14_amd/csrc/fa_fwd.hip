@@ -476,7 +476,7 @@ template <typename T, int D>
 struct SplitCfg {
   static constexpr int BC = 32;                             // keys per wave tile
   static constexpr int EPC = 16 / sizeof(T);                // elements per 16-byte chunk
-  static constexpr int KS = D + (sizeof(T) == 2 ? (D == 128 ? 24 : 8) : 4);  // padded LDS row (elements)
+  static constexpr int KS = D + (D == 128 ? 24 : 8);         // padded LDS row (elements)
   static constexpr int KCH = D / EPC;                       // 16-byte chunks per row
   static constexpr int NLD = BC * KCH / 64;                 // 16-byte loads per lane per tensor per tile
   static constexpr int TILE = BC * KS;                      // elements per K (or V) tile
@@ -488,6 +488,7 @@ struct SplitCfg {
 
 template <typename T, int D, bool DROP>
 __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
+  static_assert(sizeof(T) == 2, "16-bit inputs only: fp32 small grids take fwd_small_kernel");
   using C = SplitCfg<T, D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
@@ -515,12 +516,7 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(static_cast<const T*>(a.q) + hoff, N * RB);
   frag qf[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if constexpr (KH == 8)
-      qf[c] = __builtin_bit_cast(frag, buffer_load16(qrs, q * RB + (c * KI + hi * KH) * (int)sizeof(T)));
-    else
-      qf[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qrs, q * RB + (c * KI + hi) * 4, 0, 0));
-  }
+  for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(frag, buffer_load16(qrs, q * RB + (c * KI + hi * KH) * (int)sizeof(T)));
   uint32_t rowhash = 0;
   if constexpr (DROP) {
     const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
@@ -594,33 +590,16 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
     }
     const float base = (m_run == NEG_INF) ? 0.f : m_run;
-    uint32_t pk[8];  // 16-bit operand types: P as packed pairs
-    if constexpr (KH == 8) {
+    uint32_t pk[8];  // P as packed pairs
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p0 = exp2_fast(fmaf(sc[2 * e], a.sl2, -base));
-        const float p1 = exp2_fast(fmaf(sc[2 * e + 1], a.sl2, -base));
-        pk[e] = pack2<T>(p0, p1);
-        l_run += p0 + p1;
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pv = exp2_fast(fmaf(sc[v], a.sl2, -base));
-        l_run += pv;
-        sc[v] = pv;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float p0 = exp2_fast(fmaf(sc[2 * e], a.sl2, -base));
+      const float p1 = exp2_fast(fmaf(sc[2 * e + 1], a.sl2, -base));
+      pk[e] = pack2<T>(p0, p1);
+      l_run += p0 + p1;
     }
     const uint32_t y = DROP ? (rowhash + (uint32_t)(k0 >> 1)) * kMixMul : 0u;
-    if constexpr (DROP && KH != 8) {
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const uint32_t u = keep_finish(y + (uint32_t)(4 * (v >> 2) + ((v & 3) >> 1)) * kMixMul);
-        sc[v] = keep_lo(u, a.thresh) ? sc[v] : 0.f;
-        sc[v + 1] = keep_hi(u, a.thresh) ? sc[v + 1] : 0.f;
-      }
-    }
-    if constexpr (KH == 8) {
+    {
       const u16x2 tm1 = {(unsigned short)((a.thresh >> 16) - 1u), (unsigned short)((a.thresh >> 16) - 1u)};
       const u16x2 ones = __builtin_bit_cast(u16x2, a.ones16);
 #pragma unroll
@@ -635,13 +614,6 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
         const frag pb = frag4<T>(d4[0], d4[1], d4[2], d4[3]);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] = M::run(load_frag_tr_rp<T>(Vs, C::KS, 16 * hf, db * 32, lane), pb, o[db]);
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kk = lds_row(crow(v, hi));
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] = M::run(Vs[kk * C::KS + db * 32 + lo], sc[v], o[db]);
       }
     }
   }
@@ -693,6 +665,229 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
   }
 }
 
+// fp32 forward for grids too small to fill the device. fp32 products run on
+// the slow fp32 MFMA (64 clocks for 32x32x2), so the serial MFMA chain of a
+// wave is most of such a launch. This kernel takes 16 query rows per
+// workgroup, twice as many workgroups as the 32-row split-key kernel, with
+// v_mfma_f32_16x16x4_f32, which halves each wave's chain. As in the split-key
+// kernel the NW waves take the tiles j = w, w + NW, ... of 128 / NW keys
+// with their own LDS tiles and running (m, l), merged in LDS at the end.
+//
+// v_mfma_f32_16x16x4_f32 operands (wave64; layout checked on the device):
+// A (16 x 4): lane l holds row l % 16, k = l / 16; B (4 x 16): lane l holds
+// k = l / 16, column l % 16; C (16 x 16): lane l holds rows 4 (l / 16) + v,
+// column l % 16, for v = 0..3. Step s of a product over d takes d = 4 s +
+// l / 16 in lane l: in that order the scores come out bit-identical to the
+// 32x32x2 products (step c: d = 2 c + k) that the backward uses to recompute
+// P, so P in the backward matches the forward's to the last bit, as with
+// the other forward kernels. (Other orders round differently; against a
+// recomputed P off by rounding, fp32 gradients lose about a factor of two.)
+// S^T = K Q^T per 16-key block: A = K (row: key), B = Q^T (column: query),
+// so lane l holds keys 4 (l / 16) + v of query l % 16, and those elements are
+// directly the B operand (k = l / 16 <-> key 4 (l / 16) + v) of the
+// product O^T += V^T P^T taken one v at a time.
+template <int D, int NW>
+struct SmallCfg {
+  static constexpr int BC = 128 / NW;               // keys per wave tile (a whole number of 16-key blocks)
+  static constexpr int KB = BC / 16;
+  static constexpr int KS = D + 4;                  // LDS row stride (floats) of the K/V tiles
+  static constexpr int TILE = BC * KS;              // floats per K (or V) tile
+  static constexpr int CH = D / 4;                  // 16-byte chunks per row
+  static constexpr int NLD = BC * CH / 64;          // 16-byte loads per lane per tensor per tile
+  static constexpr int OS = D + 4;                  // fp32 row stride of the partial O
+  static constexpr int TILE_BYTES = NW * 2 * TILE * 4;
+  static constexpr int COMB_BYTES = NW * 16 * OS * 4;
+  static constexpr int BYTES = TILE_BYTES > COMB_BYTES ? TILE_BYTES : COMB_BYTES;
+};
+
+template <int D, int NW, bool DROP>
+__global__ void __launch_bounds__(64 * NW) fwd_small_kernel(AttnArgs a) {
+  using C = SmallCfg<D, NW>;
+  constexpr int BC = C::BC, KB = C::KB, NDB = D / 16, NS = D / 4;
+  constexpr int RB = D * 4;  // bytes per row
+  constexpr float NEG_INF = -__builtin_inff();
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::BYTES];
+  __shared__ float ms[NW][16], ls[NW][16], mrow[16], lrow[16];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  const int N = a.N;
+  const int nq = (N + 15) / 16;
+  const int rank = blockIdx.x / a.BH;
+  const int bh = blockIdx.x - rank * a.BH;
+  const int qt = a.causal ? (nq - 1 - rank) : rank;  // causal: longest rows first
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const float* __restrict__ Kg = static_cast<const float*>(a.k) + hoff;
+  const float* __restrict__ Vg = static_cast<const float*>(a.v) + hoff;
+  const int q0 = qt * 16;
+  const int q = q0 + c16;  // this lane's query (rows past the end read zeros; never stored)
+
+  // Q^T as the B operand: step s takes d = 4 s + g of query q.
+  const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(static_cast<const float*>(a.q) + hoff, N * RB);
+  float qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    qf[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qrs, q * RB + (4 * s + g) * 4, 0, 0));
+  uint32_t rowhash = 0;
+  if constexpr (DROP) {
+    const uint32_t hk = head_key(a.seed_lo, a.seed_hi, (uint32_t)(bh / a.H), (uint32_t)(bh % a.H));
+    rowhash = fmix32(hk ^ (uint32_t)q) + (uint32_t)(2 * g);  // keys 4g + v of a block: pairs 2g + v/2
+  }
+
+  const int kend = a.causal ? min(N, q0 + 16) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+  const uint8_t* bmrow = a.bmask ? a.bmask + (size_t)(q0 / a.mask_block) * a.nb : nullptr;
+  const bool mfew = bmrow != nullptr && a.nb <= 64;
+  const uint64_t mbits = mfew ? mask_bits(bmrow, 1, a.nb, lane) : ~0ull;
+
+  float* Ks = reinterpret_cast<float*>(smem) + w * 2 * C::TILE;  // this wave's K tile, then its V tile
+  float* Vs = Ks + C::TILE;
+
+  f32x4_t o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = NEG_INF, l_run = 0.f;
+
+  for (int j = w; j < ntiles; j += NW) {
+    if (bmrow != nullptr) {
+      const int blk = (j * BC) / a.mask_block;
+      if (mfew ? ((mbits >> blk) & 1ull) == 0 : !mask_kept(bmrow, blk)) continue;
+    }
+    const int k0 = j * BC;
+    {
+      // The wave loads its own tile (rows past the end read as zeros); LDS
+      // operations of one wave run in order, so these stores follow the
+      // reads of its previous tile and precede this tile's reads.
+      const int rem = (N - k0) * RB;
+      const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (size_t)k0 * D, rem);
+      const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (size_t)k0 * D, rem);
+      u32x4 kreg[C::NLD], vreg[C::NLD];
+#pragma unroll
+      for (int i = 0; i < C::NLD; ++i) {
+        const int c = i * 64 + lane;
+        const int off = (c / C::CH) * RB + (c % C::CH) * 16;
+        kreg[i] = buffer_load16(kr, off);
+        vreg[i] = buffer_load16(vr, off);
+      }
+#pragma unroll
+      for (int i = 0; i < C::NLD; ++i) {
+        const int c = i * 64 + lane;
+        const int e = (c / C::CH) * C::KS + (c % C::CH) * 4;
+        *reinterpret_cast<u32x4*>(&Ks[e]) = kreg[i];
+        *reinterpret_cast<u32x4*>(&Vs[e]) = vreg[i];
+      }
+    }
+    // S^T of the tile's 16-key blocks: element v of block kb is key k0 + 16 kb + 4 g + v.
+    f32x4_t sc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const float* kr = &Ks[(16 * kb + c16) * C::KS + g];  // banks 4 c16 + g: no conflicts
+#pragma unroll
+      for (int s = 0; s < NS; ++s) sc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[4 * s], qf[s], sc[kb], 0, 0, 0);
+    }
+    if ((a.causal && k0 + BC - 1 > q0) || (k0 + BC > N)) {
+      const int lim = (a.causal ? min(q, N - 1) : N - 1) - k0 - 4 * g;  // key offset 16 kb + v must not exceed it
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (16 * kb + v > lim) sc[kb][v] = NEG_INF;
+    }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sc[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // the query's maximum over the tile's 32 keys
+    const float mnew = fmaxf(m_run, mx * a.sl2);
+    if (wave_any(mnew > m_run + kLazyRescale)) {
+      const float alpha = exp2_fast(m_run - (mnew == NEG_INF ? 0.f : mnew));
+      m_run = mnew;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+    }
+    const float base = (m_run == NEG_INF) ? 0.f : m_run;
+    const uint32_t y = DROP ? (rowhash + (uint32_t)(k0 >> 1)) * kMixMul : 0u;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float pv = exp2_fast(fmaf(sc[kb][v], a.sl2, -base));
+        l_run += pv;
+        sc[kb][v] = pv;
+      }
+    if constexpr (DROP) {  // elements v, v + 1 (v even) are the two keys of pair (k0 + 16 kb + 4 g + v) / 2
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; v += 2) {
+          const uint32_t u = keep_finish(y + (uint32_t)(8 * kb + (v >> 1)) * kMixMul);
+          sc[kb][v] = keep_lo(u, a.thresh) ? sc[kb][v] : 0.f;
+          sc[kb][v + 1] = keep_hi(u, a.thresh) ? sc[kb][v + 1] : 0.f;
+        }
+    }
+    // O^T += V^T P^T, one v at a time: B = this lane's element v (k = g <-> key
+    // 16 kb + 4 g + v), A = V[that key][16 db + c16].
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float* vr = &Vs[(16 * kb + 4 * g + v) * C::KS + c16];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * db], sc[kb][v], o[db], 0, 0, 0);
+      }
+  }
+
+  // Merge the waves' partials (M = max_w m_w, a_w = 2^(m_w - M),
+  // L = sum_w a_w l_w, O = sum_w a_w O_w / L). A query's row sum is spread
+  // over the four lanes that share its column.
+  float lt = l_run + __shfl_xor(l_run, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (g == 0) {
+    ms[w][c16] = m_run;
+    ls[w][c16] = lt;
+  }
+  __syncthreads();  // every wave is done with its tiles and has posted its row statistics
+  float mall = NEG_INF;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) mall = fmaxf(mall, ms[x][c16]);
+  const float aw = (m_run == NEG_INF) ? 0.f : exp2_fast(m_run - mall);
+  float* Os = reinterpret_cast<float*>(smem) + w * 16 * C::OS;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    *reinterpret_cast<f32x4_t*>(&Os[c16 * C::OS + 16 * db + 4 * g]) = o[db] * aw;  // d = 16 db + 4 g + v'
+  if (w == 0 && g == 0) {
+    float L = 0.f;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) L += ms[x][c16] == NEG_INF ? 0.f : ls[x][c16] * exp2_fast(ms[x][c16] - mall);
+    mrow[c16] = mall;
+    lrow[c16] = L;
+  }
+  __syncthreads();
+  const float* O0 = reinterpret_cast<const float*>(smem);
+  float* __restrict__ Og = static_cast<float*>(a.out) + hoff;
+  constexpr int C4 = D / 4;  // groups of 4 columns per row
+  for (int idx = tid; idx < 16 * C4; idx += 64 * NW) {
+    const int r = idx / C4, c = (idx % C4) * 4;
+    if (q0 + r >= N) continue;
+    const float L = lrow[r];
+    const float inv = L > 0.f ? a.rp / L : 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < NW; ++x) acc += *reinterpret_cast<const f32x4_t*>(&O0[(x * 16 + r) * C::OS + c]);
+    store4<float>(Og + (size_t)(q0 + r) * D + c, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  }
+  if (tid < 16 && q0 + tid < N) {
+    const float L = lrow[tid];
+    a.lse[(size_t)bh * N + q0 + tid] = L > 0.f ? (mrow[tid] + log2_fast(L)) * kLn2 : NEG_INF;
+  }
+}
+
 // Resident waves per SIMD: with one wave, softmax VALU work, LDS reads and
 // MFMAs of a tile run back to back; more waves let them overlap. d = 128
 // fits two waves (256 VGPRs, two workgroups' LDS in the 160 KB of a CU);
@@ -708,15 +903,25 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t s) {
 }
 
 // A grid of 128-row tiles that would occupy at most a quarter of the CUs
-// takes the split-key kernel instead: four times the workgroups, each wave a
-// quarter of the keys.
+// takes a split-key kernel instead, each wave a quarter of the keys: 32-row
+// workgroups (four times the workgroups) for 16-bit inputs, 16-row ones
+// (eight times) for fp32.
 template <typename T, int D>
 static hipError_t launch_fwd_split(bool dropout, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(((a.N + 31) / 32) * a.BH));
-  if (dropout)
-    fwd_split_kernel<T, D, true><<<grid, dim3(256), 0, s>>>(a);
-  else
-    fwd_split_kernel<T, D, false><<<grid, dim3(256), 0, s>>>(a);
+  if constexpr (sizeof(T) == 4) {  // fp32: 16-row workgroups on 16x16x4 MFMAs
+    constexpr int NW = 4;  // 8 waves on 16-key tiles measured slower: the per-tile latency, not the MFMA chain, dominates there
+    const dim3 grid((unsigned)(((a.N + 15) / 16) * a.BH));
+    if (dropout)
+      fwd_small_kernel<D, NW, true><<<grid, dim3(64 * NW), 0, s>>>(a);
+    else
+      fwd_small_kernel<D, NW, false><<<grid, dim3(64 * NW), 0, s>>>(a);
+  } else {
+    const dim3 grid((unsigned)(((a.N + 31) / 32) * a.BH));
+    if (dropout)
+      fwd_split_kernel<T, D, true><<<grid, dim3(256), 0, s>>>(a);
+    else
+      fwd_split_kernel<T, D, false><<<grid, dim3(256), 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -38,9 +38,10 @@ def test_forward_small_shapes(fa, dtype, d, causal):
 
 
 # A grid of 128-row tiles that would fill at most a quarter of the CUs
-# (4 * tiles <= 256) takes the split-key kernel (32-row workgroups, the keys
-# dealt over four waves, partial results merged in LDS); the shapes above
-# mostly take it. The same cases with 68 heads take the 128-row kernel.
+# (4 * tiles <= 256) takes a split-key kernel (32-row workgroups for 16-bit
+# inputs, 16-row ones on 16x16x4 MFMAs for fp32; the keys dealt over four
+# waves, partial results merged in LDS); the shapes above mostly take it.
+# The same cases with 68 heads take the 128-row kernel.
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
@@ -49,12 +50,13 @@ def test_forward_small_shapes_wide_grid(fa, dtype, d, causal):
         _check_fwd(fa, 4, 17, N, d, dtype, causal=causal, in_seed=N + 3)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("d", [64, 128])
-def test_forward_dropout_and_block_mask_both_kernels(fa, d):
+def test_forward_dropout_and_block_mask_both_kernels(fa, dtype, d):
     N, mb = 1000, 128
     bm = random_block_mask((N + mb - 1) // mb, seed=d, frac=0.4)
     for B, H in ((1, 2), (4, 9)):  # 16 tiles (split-key kernel), 288 tiles (128-row kernel)
-        _check_fwd(fa, B, H, N, d, torch.bfloat16, causal=True, p=0.1, seed=0x5EED0003, bm=bm, mb=mb,
+        _check_fwd(fa, B, H, N, d, dtype, causal=True, p=0.1, seed=0x5EED0003, bm=bm, mb=mb,
                    in_seed=B * H + d)
 
 
