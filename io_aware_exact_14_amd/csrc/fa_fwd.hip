@@ -275,9 +275,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][kb][v]);
-        mx = half_max(mx);
-        const float mnew = fmaxf(m_run[b], mx * a.sl2);
-        if (wave_any(mnew > m_run[b] + kLazyRescale)) {
+        // A query's keys sit in two lanes. The rescale is needed iff one of
+        // them holds a score above the threshold, so the lane's own maximum
+        // decides it and the exchange of the halves runs only then.
+        if (wave_any(mx * a.sl2 > m_run[b] + kLazyRescale)) {
+          const float mnew = fmaxf(m_run[b], half_max(mx) * a.sl2);
           const float alpha = exp2_fast(m_run[b] - (mnew == NEG_INF ? 0.f : mnew));
           m_run[b] = mnew;
           l_run[b] *= alpha;
@@ -578,9 +580,8 @@ __global__ void __launch_bounds__(256) fwd_split_kernel(AttnArgs a) {
     float mx = NEG_INF;
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-    mx = half_max(mx);
-    const float mnew = fmaxf(m_run, mx * a.sl2);
-    if (wave_any(mnew > m_run + kLazyRescale)) {
+    if (wave_any(mx * a.sl2 > m_run + kLazyRescale)) {  // the exchange only when it rescales
+      const float mnew = fmaxf(m_run, half_max(mx) * a.sl2);
       const float alpha = exp2_fast(m_run - (mnew == NEG_INF ? 0.f : mnew));
       m_run = mnew;
       l_run *= alpha;
@@ -801,10 +802,10 @@ __global__ void __launch_bounds__(64 * NW) fwd_small_kernel(AttnArgs a) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sc[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // the query's maximum over the tile's 32 keys
-    const float mnew = fmaxf(m_run, mx * a.sl2);
-    if (wave_any(mnew > m_run + kLazyRescale)) {
+    if (wave_any(mx * a.sl2 > m_run + kLazyRescale)) {  // the exchanges only when it rescales
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // the query's maximum over the tile's keys
+      const float mnew = fmaxf(m_run, mx * a.sl2);
       const float alpha = exp2_fast(m_run - (mnew == NEG_INF ? 0.f : mnew));
       m_run = mnew;
       l_run *= alpha;
