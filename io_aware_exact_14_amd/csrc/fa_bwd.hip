@@ -253,7 +253,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             if (kb * 32 + 8 * (v >> 2) + (v & 3) > t) s[kb][v] = NEG_INF;
       }
       const uint32_t y = (rowhash + (uint32_t)(k0 >> 1)) * kMixMul;  // pairs k0/2 + offset: one product per tile
-      const uint32_t t16 = a.thresh >> 16;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -262,8 +261,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
           float ds = kNegD ? dp[kb][v] : dp[kb][v] + ndq;  // dP - D'
           if constexpr (DROP) {  // Z * dP - D'; elements v, v + 1 (v even) share a keep word
             const uint32_t off = (uint32_t)(kb * 16 + 4 * (v >> 2) + ((v & 3) >> 1));
-            const uint32_t u = keep_finish(y + off * kMixMul);
-            const bool keep = (v & 1) ? keep_hi(u, a.thresh) : (uint16_t)u >= (uint16_t)t16;
+            const uint32_t x = keep_mix(y + off * kMixMul);
+            const bool keep = (v & 1) ? keep_hi_mixed(x, a.thresh) : keep_lo_mixed(x, a.thresh);
             ds = keep ? ds : ndq;
           }
           s[kb][v] = p * ds;  // dS^T (times 1 - p with dropout)

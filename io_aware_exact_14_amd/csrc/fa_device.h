@@ -129,11 +129,13 @@ __device__ __forceinline__ float half_sum(float x) { return x + __shfl_xor(x, 32
 
 // MurmurHash3 32-bit finalizer (Appleby, public domain).
 constexpr uint32_t kMixMul = 0x85EBCA6Bu;  // its first multiplier
-__device__ __forceinline__ uint32_t keep_finish(uint32_t x) {  // the steps after that multiply
+__device__ __forceinline__ uint32_t keep_mix(uint32_t x) {  // the two steps after that multiply
   x ^= x >> 13;
-  x *= 0xC2B2AE35u;
-  x ^= x >> 16;
-  return x;
+  return x * 0xC2B2AE35u;
+}
+__device__ __forceinline__ uint32_t keep_finish(uint32_t x) {  // ... and the last one
+  x = keep_mix(x);
+  return x ^ (x >> 16);
 }
 __device__ __forceinline__ uint32_t fmix32(uint32_t x) { return keep_finish((x ^ (x >> 16)) * kMixMul); }
 
@@ -147,6 +149,13 @@ __device__ __forceinline__ uint32_t fmix32(uint32_t x) { return keep_finish((x ^
 // With thresh = T16 << 16 (T16 = floor(p * 2^16)): the high half is kept iff
 // u >= thresh, the low half iff (u << 16) >= thresh.
 __device__ __forceinline__ bool keep_hi(uint32_t u, uint32_t thresh) { return u >= thresh; }
+// The same two decisions from x = keep_mix(...), before the last step (u =
+// x ^ (x >> 16)): u's high half is x's, and u's low half, lo(x) ^ hi(x), is
+// the high half of x ^ (x << 16); thresh has a zero low half, so comparing
+// the whole words decides on the high halves. One operation fewer per word
+// where the two keys are tested separately.
+__device__ __forceinline__ bool keep_hi_mixed(uint32_t x, uint32_t thresh) { return x >= thresh; }
+__device__ __forceinline__ bool keep_lo_mixed(uint32_t x, uint32_t thresh) { return (x ^ (x << 16)) >= thresh; }
 
 // The same decisions for both keys of a pair at once, on the word's two
 // 16-bit halves as packed integers: half >= T16 <=> sat(half - (T16 - 1)) >= 1,
