@@ -70,7 +70,7 @@ def test_all_options_combined(fa, dtype, d, N, mb, p, gd):
                          ids=["bf16-d64-N777", "bf16-d128-N530", "f16-d64-N1111-input", "f32-d128-N333"])
 def test_all_options_at_standard_scale_fixed_bound(fa, dtype, d, N, gd):
     # causal + block mask + dropout p = 0.1 at scale 1/sqrt(d), inputs N(0,1):
-    # the benchmark spec's conditions, so the fixed bound applies with no relaxation
+    # the conditions the fixed bounds are stated for, so they apply with no relaxation
     B, H, p, seed, mb = 3, 5, 0.1, 0x5EED0003, 128
     scale = 1.0 / np.sqrt(d)
     nb = (N + mb - 1) // mb
