@@ -496,7 +496,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 
   while (it >= istart) {
     const int itn = prev_kept(it);
-    gload(itn >= istart ? itn : it);  // unconditional prefetch (see the forward kernel)
+    // Unconditional prefetch (see the forward kernel). At d = 128 it is
+    // issued after the tile's S and dP products rather than ahead of them:
+    // the products then start without waiting behind the loads' issue
+    // (dK/dV -2% at 16K keys; at d = 64 it measured even or slower, and
+    // with dropout at d = 128 it costs a spilled register).
+    constexpr bool kLateLoad = D == 128 && KH == 8 && !DROP;
+    const int itl = itn >= istart ? itn : it;
+    if constexpr (!kLateLoad) gload(itl);
     const T* Qs = &smem[cur][0];
     const T* dOs = &smem[cur][TILE];
     const int i0 = it * BR;
@@ -563,6 +570,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             else
               dp[qb] = M::run(load_frag<T>(dOs + off), vf[c], dp[qb]);
           }
+        if constexpr (kLateLoad) gload(itl);
         if (kMask == 1 || (kMask == 2 && need_mask)) {
           // Hide queries below this lane's key (causal), or every query when
           // the key is past the end: query - i0 is a compile-time offset plus
@@ -634,6 +642,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
       } else {
         step(std::integral_constant<int, 2>{});
       }
+    }
+    if constexpr (kLateLoad) {
+      if (!active) gload(itl);
     }
     sstore(cur ^ 1);
     __syncthreads();
