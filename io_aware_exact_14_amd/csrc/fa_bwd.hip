@@ -19,7 +19,7 @@
 //                   dQ^T += K^T dS^T; K^T is read from the row-major K tile
 //                   with LDS transpose reads. At d = 128 (16-bit) the K/V
 //                   tiles are loaded straight into LDS (buffer loads to LDS).
-//   bwd_dkdv_kernel one workgroup per 128 key rows: a loop over Q tiles in
+//   bwd_dkdv_kernel one workgroup per 128 (or 256) key rows: a loop over Q tiles in
 //                   the orientation S = Q K^T (lanes own a key), so P and dS
 //                   are directly the B operands of dV^T += dO^T P and
 //                   dK^T += Q^T dS; dO^T and Q^T come from the row-major
@@ -340,17 +340,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 // ---------------------------------------------------------------------------
 // VLDS: keep the workgroup's V rows in LDS (read as B fragments every tile)
 // instead of in registers, which frees 32 VGPRs per lane at d = 128.
-template <typename T, typename G, int D, int BR, bool DROP, int WPE, bool VLDS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) bwd_dkdv_kernel(AttnArgs a) {
+// NW: waves per workgroup, each owning 32 keys (BK = 32 NW keys per
+// workgroup). Eight waves (256 keys, one workgroup per CU at d = 128) share
+// each Q/dO tile between twice the keys, halving the tile loads, LDS stores
+// and barriers per key; a workgroup then spans two 128-key column blocks of
+// a block mask, so the host takes four waves when there is one.
+template <typename T, typename G, int D, int BR, bool DROP, int WPE, bool VLDS, int NW = 4>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) bwd_dkdv_kernel(AttnArgs a) {
+  constexpr int NT = 64 * NW;
   using S = TileShape<T, D>;
   using M = Mfma<T>;
   using frag = typename M::frag;
   constexpr int KI = M::KI, KH = M::KH;
-  constexpr int BK = 128;  // keys per workgroup
+  constexpr int BK = 32 * NW;  // keys per workgroup
   constexpr int NQB = BR / 32, NDB = D / 32, NC = D / KI;
-  constexpr int NLD = BR * S::KCH / 256;
+  constexpr int NLD = BR * S::KCH / NT;
   constexpr int TILE = BR * S::RS;
-  static_assert((BR * S::KCH) % 256 == 0 && BR <= 256 && BK % BR == 0, "tile shape");
+  static_assert((BR * S::KCH) % NT == 0 && BR <= NT && BK % BR == 0, "tile shape");
   constexpr float NEG_INF = -__builtin_inff(), POS_INF = __builtin_inff();
 
   __shared__ __attribute__((aligned(16))) T smem[2][2 * TILE];  // [buffer][Q tile | dO tile]
@@ -401,10 +407,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     if constexpr (!VLDS) vf[c] = load_frag<T>(Vg + off);
   }
   if constexpr (VLDS) {
-    constexpr int NLV = BK * S::KCH / 256;
+    constexpr int NLV = BK * S::KCH / NT;
 #pragma unroll
     for (int i = 0; i < NLV; ++i) {
-      const int c = i * 256 + tid;
+      const int c = i * NT + tid;
       const int row = c / S::KCH, ch = c % S::KCH;
       *reinterpret_cast<u32x4*>(&vsm[row * S::KS + ch * S::EPC]) =
           *reinterpret_cast<const u32x4*>(Vg + (size_t)min(k0wg + row, N - 1) * D + ch * S::EPC);
@@ -448,8 +454,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const __amdgpu_buffer_rsrc_t orr = buffer_rsrc(dOg + (size_t)i0 * D, rem);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {  // chunk c = row c / KCH, 16-byte piece c % KCH
-      qreg[i] = buffer_load16(qr, (i * 256 + tid) * 16);
-      oreg[i] = buffer_load16(orr, (i * 256 + tid) * 16);
+      qreg[i] = buffer_load16(qr, (i * NT + tid) * 16);
+      oreg[i] = buffer_load16(orr, (i * NT + tid) * 16);
     }
     // Row statistics of the tile: every lane loads, lanes < BR keep. Padding
     // rows (and rows with no valid key) get log2-LSE = +inf, so P = 0.
@@ -464,7 +470,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int c = i * 256 + tid;
+      const int c = i * NT + tid;
       const int row = lds_row(c / S::KCH), ch = c % S::KCH;
       *reinterpret_cast<u32x4*>(&smem[buf][row * S::KS + ch * S::EPC]) = qreg[i];
       *reinterpret_cast<u32x4*>(&smem[buf][TILE + row * S::KS + ch * S::EPC]) = oreg[i];
@@ -662,6 +668,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     // distinct bank quads.
     constexpr int RS = D + 4;
     constexpr int WAVE_FLOATS = 32 * RS;
+    static_assert(NW == 4, "the staging areas below hold four waves' rows");
     static_assert(sizeof(smem) >= (VLDS ? 2 : 4) * WAVE_FLOATS * sizeof(float), "staging space in the tile buffers");
     static_assert(!VLDS || sizeof(vsm) >= 2 * WAVE_FLOATS * sizeof(float), "staging space in the V rows");
     float* st;
@@ -715,7 +722,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 // (causal rows of at most a few thousand keys) run few tiles per workgroup,
 // so they take small tiles and high occupancy; long ones take larger tiles,
 // which amortize the per-tile barrier and loads. With VLDS the dK/dV kernel
-// keeps the workgroup's V rows in LDS instead of registers.
+// keeps the workgroup's V rows in LDS instead of registers. At d = 128 the
+// dK/dV kernel runs eight waves (256 keys) per workgroup unless a block mask
+// is given (C4 dK/dV -2.7%); at d = 64 eight waves measured slower (+6% at
+// 4096 keys with 64-row tiles) and the d = 64 epilogue stages four waves.
 template <typename T, typename G, int D, bool DROP, int BC, int WPE>
 static hipError_t launch_dq(const AttnArgs& a, hipStream_t s) {
   const int nt = (a.N + 127) / 128;
@@ -723,10 +733,10 @@ static hipError_t launch_dq(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, typename G, int D, bool DROP, int BR, int WPE, bool VLDS>
+template <typename T, typename G, int D, bool DROP, int BR, int WPE, bool VLDS, int NW = 4>
 static hipError_t launch_dkdv(const AttnArgs& a, hipStream_t s) {
-  const int nt = (a.N + 127) / 128;
-  bwd_dkdv_kernel<T, G, D, BR, DROP, WPE, VLDS><<<dim3((unsigned)(nt * a.BH)), dim3(256), 0, s>>>(a);
+  const int nt = (a.N + 32 * NW - 1) / (32 * NW);
+  bwd_dkdv_kernel<T, G, D, BR, DROP, WPE, VLDS, NW><<<dim3((unsigned)(nt * a.BH)), dim3(64 * NW), 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -747,7 +757,7 @@ static hipError_t launch_bwd_cfg(int stage, const AttnArgs& a, hipStream_t s) {
     if constexpr (!h)
       e = launch_dkdv<T, G, D, DROP, D == 64 ? 64 : 32, 1, false>(a, s);
     else if constexpr (D == 128)
-      e = launch_dkdv<T, G, D, DROP, 32, 2, true>(a, s);
+      e = a.bmask ? launch_dkdv<T, G, D, DROP, 32, 2, true>(a, s) : launch_dkdv<T, G, D, DROP, 32, 2, true, 8>(a, s);
     else
       e = a.N <= 2048 ? launch_dkdv<T, G, D, DROP, 32, DROP ? 2 : 3, true>(a, s)
                       : launch_dkdv<T, G, D, DROP, 64, 2, false>(a, s);
