@@ -42,6 +42,9 @@ def test_backward_small_shapes(fa, dtype, d, causal):
 def test_backward_tails_and_multiple_tiles(fa, N):
     _check_bwd(fa, 2, 2, N, 64, torch.bfloat16, causal=True, in_seed=N)
     _check_bwd(fa, 1, 2, N, 128, torch.bfloat16, causal=False, in_seed=N + 1)
+    # d = 128 causal: 256-key dK/dV workgroups whose diagonal rows leave
+    # some waves idle, and a ragged last key block
+    _check_bwd(fa, 1, 3, N, 128, torch.bfloat16, causal=True, in_seed=N + 2)
 
 
 def test_backward_causal_sixteen_heads_ragged(fa):
