@@ -5,7 +5,7 @@
     python bench.py --workload C2 --only           one workload (profiling runs)
     python bench.py --standard [--workload C2]     standard vs tiled attention
     python bench.py --sweep [--sweep-n 1024,...]   sequence-length sweep
-    python bench.py --roofs                        MFMA / VALU / LDS / HBM / launch microbenchmarks
+    python bench.py --roofs                        MFMA / VALU / LDS / tile skeleton / HBM / launch microbenchmarks
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 fa_fwd (O, LSE), then the two backward stages fa_bwd_dq (D, dQ) and
@@ -714,8 +714,8 @@ def run_roofs(args):
     """Microbenchmarks of the roofs the kernels are measured against (HIP
     kernels in the package's roofs library): MFMA rate and the clock it runs
     at, issue rates of the VALU instructions the kernels use, MFMA / VALU
-    overlap, LDS read bandwidth (plain and transpose reads), HBM copy and the
-    empty-launch floor."""
+    overlap, LDS read bandwidth (plain and transpose reads), the compute
+    skeleton of a forward tile step, HBM copy and the empty-launch floor."""
     import torch
 
     from io_aware_exact_14_amd import roofs
@@ -743,7 +743,7 @@ def main():
                     help="run one 512 MiB device copy first (reference kernel for HBM counters)")
     ap.add_argument("--standard", action="store_true", help="standard vs tiled attention on --workload")
     ap.add_argument("--sweep", action="store_true", help="sequence-length sweep of the tiled kernels")
-    ap.add_argument("--roofs", action="store_true", help="MFMA / VALU / LDS / HBM / launch microbenchmarks")
+    ap.add_argument("--roofs", action="store_true", help="MFMA / VALU / LDS / tile skeleton / HBM / launch microbenchmarks")
     ap.add_argument("--sweep-n", default="1024,2048,4096,8192,16384,32768,65536")
     ap.add_argument("--sweep-d", default="64,128")
     ap.add_argument("--sweep-tokens", type=int, default=16384, help="B = max(1, tokens // N)")

@@ -1,7 +1,8 @@
 """Python driver of libfa_roofs.so: microbenchmarks of the roofs the
 attention kernels are measured against (bf16 MFMA rate and its clock,
 issue rates of the VALU instructions the kernels use, MFMA / VALU overlap,
-LDS read bandwidth, HBM copy, empty-launch floor).
+LDS read bandwidth, the compute skeleton of a forward tile step, HBM copy,
+empty-launch floor).
 
 Used by ``bench.py --roofs``. The library is built beside libfa.so by
 ``build.py``; it is measurement tooling, not part of the attention path.
@@ -25,7 +26,9 @@ def _load():
     lib.roofs_overlap.argtypes = [ctypes.c_int, ctypes.c_int, d, d]
     lib.roofs_copy.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, d, d]
     lib.roofs_launch.argtypes = [ctypes.c_int, ctypes.c_int, d]
-    for f in (lib.roofs_mfma, lib.roofs_valu, lib.roofs_lds, lib.roofs_overlap, lib.roofs_copy, lib.roofs_launch):
+    lib.roofs_skeleton.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, d, d]
+    for f in (lib.roofs_mfma, lib.roofs_valu, lib.roofs_lds, lib.roofs_overlap, lib.roofs_copy, lib.roofs_launch,
+              lib.roofs_skeleton):
         f.restype = ctypes.c_int
     return lib
 
@@ -81,6 +84,16 @@ def run_all(cus: int | None = None) -> dict:
             out["lds_clock_ghz"] = round(clk.value, 4)
             out["lds_ms"] = round(ms.value, 3)
         out[f"{name}_bytes_per_clk_per_cu"] = round(r.value / (cus * clk.value * 1e9), 1)
+    for dh in (64, 128):
+        for lds in (0, 1):
+            cyc, clk = _d(), _d()
+            if lib.roofs_skeleton(dh, lds, 4000, ctypes.byref(cyc), ctypes.byref(clk)) != 0:
+                raise RuntimeError("roofs_skeleton failed")
+            tag = f"skeleton_d{dh}_{'lds' if lds else 'regs'}"
+            out[f"{tag}_cycles_per_tile"] = round(cyc.value, 1)
+            # products per wave tile: 2 * d/16 (S) + 4 * d/32 (PV), 32 matrix-pipe cycles each
+            out[f"{tag}_mfma_frac"] = round(32.0 * (2 * dh // 16 + 4 * dh // 32) / cyc.value, 3)
+            out[f"{tag}_clock_ghz"] = round(clk.value, 4)
     best = None
     for bpc in (2, 8, 32):
         for unr in (1, 4, 8):
@@ -102,7 +115,11 @@ def run_all(cus: int | None = None) -> dict:
                     "instruction per SIMD (pairs: per two-instruction step). Overlap: 2 independent MFMAs (64 "
                     "matrix-pipe cycles) plus n FMAs per iteration, SIMD cycles per wave iteration at 4 waves "
                     "per SIMD. LDS: ds_read_b128 of consecutive 16-byte chunks, and two ds_read_b64_tr_b16 per "
-                    "lane in the kernels' transpose pattern (64-row bf16 tile, 144-byte rows), 4 waves per SIMD. HBM: 1 GiB device copy (read + write bytes counted), nontemporal "
+                    "lane in the kernels' transpose pattern (64-row bf16 tile, 144-byte rows), 4 waves per SIMD. Skeleton: a "
+                    "forward tile step (32 queries x 64 keys per wave: S products, FMA + exp2 + bf16 pack + row "
+                    "sum on 32 scores per lane, PV products) with no HBM traffic, K/V operands from registers or "
+                    "from an LDS tile written once, 4 waves per SIMD at d=64 and 2 at d=128; SIMD cycles per wave "
+                    "tile step and the matrix pipe's share of them. HBM: 1 GiB device copy (read + write bytes counted), nontemporal "
                     "loads and stores, workgroups per CU x 16-byte elements per lane per step swept. Launch: 200 "
                     "back-to-back launches of an empty kernel (1, 4 or 1024 workgroups) between one event pair.")
     return out

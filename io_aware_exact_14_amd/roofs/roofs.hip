@@ -1,7 +1,8 @@
 // Microbenchmarks of the MI355X roofs that the attention kernels are measured
 // against: bf16 MFMA rate and the shader clock it runs at, issue rates of the
 // VALU instructions the kernels use, MFMA / VALU overlap, LDS read bandwidth
-// (plain and transpose reads), an HBM copy and the empty-launch floor. Each entry point
+// (plain and transpose reads), the compute skeleton of a forward tile step,
+// an HBM copy and the empty-launch floor. Each entry point
 // runs one timed launch (after one warm-up launch) on the current device and
 // returns its results through pointers; every loop has a fixed trip count and
 // every access stays inside the buffers the entry point allocates.
@@ -187,6 +188,98 @@ __global__ void __launch_bounds__(256) lds_tr_kernel(float* out, int iters, unsi
   out[blockIdx.x * 256 + threadIdx.x] = (float)(a0 + a1);
 }
 
+// Compute skeleton of one forward tile step of the attention kernels, with
+// no HBM traffic: per iteration a wave forms S^T (2 key blocks of 32 x its
+// 32 queries, D/16 steps each), the softmax arithmetic of its 32 scores per
+// lane (FMA, exp2, pairwise bf16 pack, row sum) and O^T += V^T P^T
+// (D/32 x 4 products). USE_LDS reads the K fragments (ds_read_b128) and the
+// V^T fragments (ds_read_b64_tr_b16 pairs) from one of two 64-key LDS tiles
+// written once before the loop, alternating per step as in the kernels'
+// double buffer (so the reads stay inside the loop), with the kernels'
+// padded row strides; otherwise the operands come from registers. WPE waves per SIMD. This bounds what the
+// tile loop can reach when tile loads, stores, masking and barriers cost
+// nothing.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <int D, int WPE, bool USE_LDS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
+skeleton_kernel(float* out, int iters, float sl2, unsigned long long* stamps) {
+  constexpr int KS = D + (D == 128 ? 24 : 8), NC = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 kt[USE_LDS ? 2 * 64 * KS : 8];
+  __shared__ __attribute__((aligned(16))) __bf16 vt[USE_LDS ? 2 * 64 * KS : 8];
+  const int tid = threadIdx.x, lane = tid & 63, lo = lane & 31, hi = lane >> 5, j = lane & 15;
+  if (USE_LDS) {
+    for (int i = tid; i < 2 * 64 * KS; i += 256) {
+      kt[i] = (__bf16)(0.001f * (float)(i % 97));
+      vt[i] = (__bf16)(0.002f * (float)(i % 89));
+    }
+  }
+  __syncthreads();
+  bf16x8 q[NC], k1[USE_LDS ? 1 : NC];  // k1: the second key block's operands in the register variant
+  for (int c = 0; c < NC; ++c)
+    for (int i = 0; i < 8; ++i) q[c][i] = (__bf16)(0.001f * (float)(tid + i + c));
+  if (!USE_LDS)
+    for (int c = 0; c < NC; ++c)
+      for (int i = 0; i < 8; ++i) k1[c][i] = (__bf16)(0.003f * (float)(tid - i + 2 * c));
+  f32x16 o[NDB] = {};
+  float l = 0.f;
+  const Stamp s0 = stamp_now();
+  for (int it = 0; it < iters; ++it) {
+    const int t0 = (it & 1) * 64 * KS;  // this step's tile
+    f32x16 s[2] = {};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 kf;
+        if constexpr (USE_LDS)  // row kb*32 + lo, columns 16c + 8hi .. + 7: inside the 64 x KS tile
+          kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_t*>(&kt[t0 + (kb * 32 + lo) * KS + c * 16 + hi * 8]));
+        else
+          kf = kb ? k1[USE_LDS ? 0 : c] : q[c];  // distinct per key block (no common subexpression)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q[c], s[kb], 0, 0, 0);
+      }
+    uint32_t pk[16];
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * e], sl2, -1.f));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * e + 1], sl2, -1.f));
+        pk[kb * 8 + e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+        rs += p0 + p1;
+      }
+    l += rs;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4_t{pk[kb * 8 + 4 * hf], pk[kb * 8 + 4 * hf + 1],
+                                                            pk[kb * 8 + 4 * hf + 2], pk[kb * 8 + 4 * hf + 3]});
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          bf16x8 vf;
+          if constexpr (USE_LDS) {  // rows kb*32 + 16hf + 4hi + j/4 (and + 8) <= 63, columns < 32db + 32
+            const __bf16* pp = &vt[t0 + (kb * 32 + 16 * hf + 4 * hi + (j >> 2)) * KS + db * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3)];
+            const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)pp);
+            const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pp + 8 * KS));
+            vf = __builtin_bit_cast(bf16x8, i16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]});
+          } else {
+            vf = q[db];
+          }
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, b, o[db], 0, 0, 0);
+        }
+      }
+  }
+  stamp_store(stamps, s0, stamp_now());
+  float sm = l;
+  for (int db = 0; db < NDB; ++db)
+    for (int i = 0; i < 16; ++i) sm += o[db][i];
+  out[blockIdx.x * 256 + threadIdx.x] = sm;
+}
+
 // An empty kernel: the floor of a launch that depends on the previous one.
 __global__ void __launch_bounds__(256) empty_kernel(int* out) {
   if (out != nullptr && threadIdx.x == 0 && blockIdx.x == 0x7fffffff) out[0] = 0;
@@ -339,6 +432,37 @@ int roofs_overlap(int nv, int iters, double* cycles, double* clock_ghz) {
   (void)hipFree(st);
   if (ms <= 0.0) return 3;
   *cycles = *clock_ghz * 1e9 * ms * 1e-3 / (4.0 * iters);
+  return 0;
+}
+
+// skeleton_kernel at head dimension d (64 at 4 waves per SIMD, 128 at 2),
+// operands from LDS or registers: SIMD cycles per wave tile step, and the
+// clock.
+int roofs_skeleton(int d, int use_lds, int iters, double* cycles, double* clock_ghz) {
+  const int cus = device_cus();
+  if (cus <= 0 || iters <= 0 || (d != 64 && d != 128)) return 1;
+  const int wpe = d == 64 ? 4 : 2;
+  const int blocks = cus * wpe;
+  float* out = nullptr;
+  unsigned long long* st = nullptr;
+  if (hipMalloc(&out, (size_t)blocks * 256 * sizeof(float)) != hipSuccess) return 2;
+  if (hipMalloc(&st, 2 * sizeof(unsigned long long)) != hipSuccess) return 2;
+  const float sl2 = 0.18f;
+  const double ms = timed([&] {
+    if (d == 64 && use_lds)
+      skeleton_kernel<64, 4, true><<<blocks, 256>>>(out, iters, sl2, st);
+    else if (d == 64)
+      skeleton_kernel<64, 4, false><<<blocks, 256>>>(out, iters, sl2, st);
+    else if (use_lds)
+      skeleton_kernel<128, 2, true><<<blocks, 256>>>(out, iters, sl2, st);
+    else
+      skeleton_kernel<128, 2, false><<<blocks, 256>>>(out, iters, sl2, st);
+  });
+  *clock_ghz = stamp_ghz(st);
+  (void)hipFree(out);
+  (void)hipFree(st);
+  if (ms <= 0.0) return 3;
+  *cycles = *clock_ghz * 1e9 * ms * 1e-3 / ((double)wpe * iters);
   return 0;
 }
 
