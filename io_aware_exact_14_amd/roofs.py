@@ -26,7 +26,7 @@ def _load():
     lib.roofs_overlap.argtypes = [ctypes.c_int, ctypes.c_int, d, d]
     lib.roofs_copy.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, d, d]
     lib.roofs_launch.argtypes = [ctypes.c_int, ctypes.c_int, d]
-    lib.roofs_skeleton.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, d, d]
+    lib.roofs_skeleton.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, d, d]
     for f in (lib.roofs_mfma, lib.roofs_valu, lib.roofs_lds, lib.roofs_overlap, lib.roofs_copy, lib.roofs_launch,
               lib.roofs_skeleton):
         f.restype = ctypes.c_int
@@ -85,11 +85,11 @@ def run_all(cus: int | None = None) -> dict:
             out["lds_ms"] = round(ms.value, 3)
         out[f"{name}_bytes_per_clk_per_cu"] = round(r.value / (cus * clk.value * 1e9), 1)
     for dh in (64, 128):
-        for lds in (0, 1):
+        for lds, pipe in ((0, 0), (1, 0)) + (((0, 1), (1, 1)) if dh == 128 else ()):
             cyc, clk = _d(), _d()
-            if lib.roofs_skeleton(dh, lds, 4000, ctypes.byref(cyc), ctypes.byref(clk)) != 0:
+            if lib.roofs_skeleton(dh, lds, pipe, 4000, ctypes.byref(cyc), ctypes.byref(clk)) != 0:
                 raise RuntimeError("roofs_skeleton failed")
-            tag = f"skeleton_d{dh}_{'lds' if lds else 'regs'}"
+            tag = f"skeleton_d{dh}_{'lds' if lds else 'regs'}{'_pipelined' if pipe else ''}"
             out[f"{tag}_cycles_per_tile"] = round(cyc.value, 1)
             # products per wave tile: 2 * d/16 (S) + 4 * d/32 (PV), 32 matrix-pipe cycles each
             out[f"{tag}_mfma_frac"] = round(32.0 * (2 * dh // 16 + 4 * dh // 32) / cyc.value, 3)
@@ -118,8 +118,10 @@ def run_all(cus: int | None = None) -> dict:
                     "lane in the kernels' transpose pattern (64-row bf16 tile, 144-byte rows), 4 waves per SIMD. Skeleton: a "
                     "forward tile step (32 queries x 64 keys per wave: S products, FMA + exp2 + bf16 pack + row "
                     "sum on 32 scores per lane, PV products) with no HBM traffic, K/V operands from registers or "
-                    "from an LDS tile written once, 4 waves per SIMD at d=64 and 2 at d=128; SIMD cycles per wave "
-                    "tile step and the matrix pipe's share of them. HBM: 1 GiB device copy (read + write bytes counted), nontemporal "
+                    "from an LDS tile written once, 4 waves per SIMD at d=64 and 2 at d=128, plain or (d=128) software-"
+                    "pipelined (the next step's S products issued between this step's exponentials, fenced, K "
+                    "fragments read three products ahead); SIMD cycles per wave tile step and the matrix pipe's "
+                    "share of them. HBM: 1 GiB device copy (read + write bytes counted), nontemporal "
                     "loads and stores, workgroups per CU x 16-byte elements per lane per step swept. Launch: 200 "
                     "back-to-back launches of an empty kernel (1, 4 or 1024 workgroups) between one event pair.")
     return out

@@ -196,14 +196,15 @@ __global__ void __launch_bounds__(256) lds_tr_kernel(float* out, int iters, unsi
 // V^T fragments (ds_read_b64_tr_b16 pairs) from one of two 64-key LDS tiles
 // written once before the loop, alternating per step as in the kernels'
 // double buffer (so the reads stay inside the loop), with the kernels'
-// padded row strides; otherwise the operands come from registers. WPE waves per SIMD. This bounds what the
-// tile loop can reach when tile loads, stores, masking and barriers cost
-// nothing.
+// padded row strides; otherwise the operands come from registers. WPE waves
+// per SIMD. This bounds what the tile loop can reach when tile loads, stores,
+// masking and barriers cost nothing. PIPE software-pipelines the step: the
+// next step's S products are issued between this step's exponentials.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-template <int D, int WPE, bool USE_LDS>
+template <int D, int WPE, bool USE_LDS, bool PIPE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 skeleton_kernel(float* out, int iters, float sl2, unsigned long long* stamps) {
   constexpr int KS = D + (D == 128 ? 24 : 8), NC = D / 16, NDB = D / 32;
@@ -223,34 +224,71 @@ skeleton_kernel(float* out, int iters, float sl2, unsigned long long* stamps) {
   if (!USE_LDS)
     for (int c = 0; c < NC; ++c)
       for (int i = 0; i < 8; ++i) k1[c][i] = (__bf16)(0.003f * (float)(tid - i + 2 * c));
+  // K fragment of key block kb, d step c, from the tile at element offset t0
+  // (row kb*32 + lo, columns 16c + 8hi .. + 7: inside the 64 x KS tile).
+  auto kfrag = [&](int t0, int kb, int c) {
+    if constexpr (USE_LDS)
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_t*>(&kt[t0 + (kb * 32 + lo) * KS + c * 16 + hi * 8]));
+    else
+      return kb ? k1[USE_LDS ? 0 : c] : q[c];  // distinct per key block (no common subexpression)
+  };
   f32x16 o[NDB] = {};
+  f32x16 sn[2] = {};  // PIPE: the next step's scores
   float l = 0.f;
-  const Stamp s0 = stamp_now();
-  for (int it = 0; it < iters; ++it) {
-    const int t0 = (it & 1) * 64 * KS;  // this step's tile
-    f32x16 s[2] = {};
+  if constexpr (PIPE) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 kf;
-        if constexpr (USE_LDS)  // row kb*32 + lo, columns 16c + 8hi .. + 7: inside the 64 x KS tile
-          kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_t*>(&kt[t0 + (kb * 32 + lo) * KS + c * 16 + hi * 8]));
-        else
-          kf = kb ? k1[USE_LDS ? 0 : c] : q[c];  // distinct per key block (no common subexpression)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q[c], s[kb], 0, 0, 0);
-      }
+      for (int kb = 0; kb < 2; ++kb) sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(0, kb, c), q[c], sn[kb], 0, 0, 0);
+  }
+  const Stamp s0 = stamp_now();
+  for (int it = 0; it < iters; ++it) {
+    const int t0 = (it & 1) * 64 * KS;  // this step's tile
     uint32_t pk[16];
     float rs = 0.f;
+    if constexpr (!PIPE) {
+      f32x16 s[2] = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * e], sl2, -1.f));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * e + 1], sl2, -1.f));
-        pk[kb * 8 + e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
-        rs += p0 + p1;
+        for (int kb = 0; kb < 2; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(t0, kb, c), q[c], s[kb], 0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * e], sl2, -1.f));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * e + 1], sl2, -1.f));
+          pk[kb * 8 + e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+          rs += p0 + p1;
+        }
+    } else {
+      // The next step's S products (from the other tile), one per chunk,
+      // between this step's exponentials; K fragments read three products
+      // ahead; sched_barrier fences keep the order.
+      const f32x16 s[2] = {sn[0], sn[1]};
+      sn[0] = f32x16{};
+      sn[1] = f32x16{};
+      const int t1 = ((it + 1) & 1) * 64 * KS;
+      constexpr int NP = 2 * NC, E = 16 / NP, LA = 3;  // products, score pairs per product, lookahead
+      bf16x8 kq[NP];
+#pragma unroll
+      for (int i = 0; i < LA; ++i) kq[i] = kfrag(t1, i & 1, i >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        if (i + LA < NP) kq[i + LA] = kfrag(t1, (i + LA) & 1, (i + LA) >> 1);
+        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[i], q[i >> 1], sn[i & 1], 0, 0, 0);
+#pragma unroll
+        for (int e2 = 0; e2 < E; ++e2) {
+          const int pe = i * E + e2, kb = pe >> 3, e = pe & 7;  // score pair pe of 16
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * e], sl2, -1.f));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * e + 1], sl2, -1.f));
+          pk[pe] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+          rs += p0 + p1;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
     l += rs;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -274,7 +312,7 @@ skeleton_kernel(float* out, int iters, float sl2, unsigned long long* stamps) {
       }
   }
   stamp_store(stamps, s0, stamp_now());
-  float sm = l;
+  float sm = l + sn[0][0] + sn[1][1];
   for (int db = 0; db < NDB; ++db)
     for (int i = 0; i < 16; ++i) sm += o[db][i];
   out[blockIdx.x * 256 + threadIdx.x] = sm;
@@ -436,11 +474,13 @@ int roofs_overlap(int nv, int iters, double* cycles, double* clock_ghz) {
 }
 
 // skeleton_kernel at head dimension d (64 at 4 waves per SIMD, 128 at 2),
-// operands from LDS or registers: SIMD cycles per wave tile step, and the
-// clock.
-int roofs_skeleton(int d, int use_lds, int iters, double* cycles, double* clock_ghz) {
+// operands from LDS or registers, plain or software-pipelined: SIMD cycles
+// per wave tile step, and the clock.
+int roofs_skeleton(int d, int use_lds, int pipe, int iters, double* cycles, double* clock_ghz) {
   const int cus = device_cus();
-  if (cus <= 0 || iters <= 0 || (d != 64 && d != 128)) return 1;
+  // The pipelined step needs a second score tile, beyond the 128 registers
+  // of four waves per SIMD at d = 64, so it is measured at d = 128 only.
+  if (cus <= 0 || iters <= 0 || (d != 64 && d != 128) || (pipe && d == 64)) return 1;
   const int wpe = d == 64 ? 4 : 2;
   const int blocks = cus * wpe;
   float* out = nullptr;
@@ -448,15 +488,16 @@ int roofs_skeleton(int d, int use_lds, int iters, double* cycles, double* clock_
   if (hipMalloc(&out, (size_t)blocks * 256 * sizeof(float)) != hipSuccess) return 2;
   if (hipMalloc(&st, 2 * sizeof(unsigned long long)) != hipSuccess) return 2;
   const float sl2 = 0.18f;
+  const int sel = (d == 128 ? 4 : 0) + (use_lds ? 2 : 0) + (pipe ? 1 : 0);
   const double ms = timed([&] {
-    if (d == 64 && use_lds)
-      skeleton_kernel<64, 4, true><<<blocks, 256>>>(out, iters, sl2, st);
-    else if (d == 64)
-      skeleton_kernel<64, 4, false><<<blocks, 256>>>(out, iters, sl2, st);
-    else if (use_lds)
-      skeleton_kernel<128, 2, true><<<blocks, 256>>>(out, iters, sl2, st);
-    else
-      skeleton_kernel<128, 2, false><<<blocks, 256>>>(out, iters, sl2, st);
+    switch (sel) {
+      case 0: skeleton_kernel<64, 4, false, false><<<blocks, 256>>>(out, iters, sl2, st); break;
+      case 2: skeleton_kernel<64, 4, true, false><<<blocks, 256>>>(out, iters, sl2, st); break;
+      case 4: skeleton_kernel<128, 2, false, false><<<blocks, 256>>>(out, iters, sl2, st); break;
+      case 5: skeleton_kernel<128, 2, false, true><<<blocks, 256>>>(out, iters, sl2, st); break;
+      case 6: skeleton_kernel<128, 2, true, false><<<blocks, 256>>>(out, iters, sl2, st); break;
+      default: skeleton_kernel<128, 2, true, true><<<blocks, 256>>>(out, iters, sl2, st); break;
+    }
   });
   *clock_ghz = stamp_ghz(st);
   (void)hipFree(out);
