@@ -185,6 +185,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   // Direct-to-LDS variant: lane L of wave w fills LDS chunk i*256 + 64*w + L
   // (row c / KCH, physical chunk c % KCH) with the logical chunk the swizzle
   // puts there; rows past the end read as zeros (their scores are masked).
+  // The wave index in a scalar register: each load's LDS address (M0) is
+  // then scalar arithmetic rather than a vector value moved per load.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   auto dma = [&](int jt, int buf) {
     const int k0 = jt * BC;
     const int rem = (N - k0) * D * (int)sizeof(T);
@@ -192,7 +195,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (size_t)k0 * D, rem);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int c = i * 256 + tid, c0 = i * 256 + w * 64;
+      const int c = i * 256 + tid, c0 = i * 256 + wu * 64;
       const int row = c / S::KCH;
       const int voff = (row * S::KCH + ((c % S::KCH) ^ lds_swizzle<D>(row))) * 16;
       buffer_load16_lds(kr, &smem[buf][c0 * S::EPC], voff);

@@ -159,6 +159,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   // 16-bit: K and V tiles go straight from HBM into LDS buffer `buf`; lane L
   // of wave w fills LDS chunk i*256 + 64*w + L, i.e. row c / KCH and physical
   // chunk c % KCH, with the logical chunk that the swizzle places there.
+  // The wave index is read into a scalar register, so each load's LDS
+  // address (M0) is scalar arithmetic rather than a vector value moved to a
+  // scalar register per load.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   auto dma = [&](int jt, int buf) {
     const int k0 = jt * BC;
     const int rem = (N - k0) * RB;
@@ -166,7 +170,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (size_t)k0 * D, rem);
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i) {
-      const int c0 = i * 256 + w * 64;  // first chunk this wave writes
+      const int c0 = i * 256 + wu * 64;  // first chunk this wave writes
       buffer_load16_lds(kr, &smem[buf][c0 * C::EPC], voff[i]);
       buffer_load16_lds(vr, &smem[buf][C::TILE + c0 * C::EPC], voff[i]);
     }
