@@ -83,7 +83,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   static_assert((BC * S::KCH) % 256 == 0, "tile shape");
   constexpr float NEG_INF = -__builtin_inff(), POS_INF = __builtin_inff();
 
-  __shared__ __attribute__((aligned(16))) T smem[2][2 * TILE];  // [buffer][K tile | V tile]
+  // Two tile buffers [K tile | V tile] as separate arrays, with the tile
+  // loop unrolled by two, as in the forward kernel: the compiler then tells
+  // the direct-to-LDS loads into one buffer from the reads of the other.
+  __shared__ __attribute__((aligned(16))) T smem0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) T smem1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lo = lane & 31, hi = lane >> 5;
@@ -173,13 +177,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
       vreg[i] = buffer_load16(vr, (i * 256 + tid) * 16);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](T* dst) {
 #pragma unroll
     for (int i = 0; i < (S::DMA ? 1 : NLD); ++i) {
       const int c = i * 256 + tid;
       const int row = lds_row(c / S::KCH), ch = c % S::KCH;
-      *reinterpret_cast<u32x4*>(&smem[buf][row * S::KS + ch * S::EPC]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&smem[buf][TILE + row * S::KS + ch * S::EPC]) = vreg[i];
+      *reinterpret_cast<u32x4*>(dst + row * S::KS + ch * S::EPC) = kreg[i];
+      *reinterpret_cast<u32x4*>(dst + TILE + row * S::KS + ch * S::EPC) = vreg[i];
     }
   };
   // Direct-to-LDS variant: lane L of wave w fills LDS chunk i*256 + 64*w + L
@@ -188,7 +192,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   // The wave index in a scalar register: each load's LDS address (M0) is
   // then scalar arithmetic rather than a vector value moved per load.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto dma = [&](int jt, int buf) {
+  auto dma = [&](int jt, T* dst) {
     const int k0 = jt * BC;
     const int rem = (N - k0) * D * (int)sizeof(T);
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (size_t)k0 * D, rem);
@@ -198,8 +202,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
       const int c = i * 256 + tid, c0 = i * 256 + wu * 64;
       const int row = c / S::KCH;
       const int voff = (row * S::KCH + ((c % S::KCH) ^ lds_swizzle<D>(row))) * 16;
-      buffer_load16_lds(kr, &smem[buf][c0 * S::EPC], voff);
-      buffer_load16_lds(vr, &smem[buf][TILE + c0 * S::EPC], voff);
+      buffer_load16_lds(kr, dst + c0 * S::EPC, voff);
+      buffer_load16_lds(vr, dst + TILE + c0 * S::EPC, voff);
     }
   };
 
@@ -207,27 +211,36 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = zero16();
 
+  // Lane parts of the K^T transpose-read addresses (swizzled tiles).
+  int2 trl[S::DMA ? NDB : 1];
+  if constexpr (S::DMA) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) trl[db] = tr_swz_lane<T, D>(db * 32, lane);
+  }
+
   int j = kept(0) ? 0 : next_kept(0);
-  int cur = 0;
   if (j < ntiles) {
     if constexpr (S::DMA) {
-      dma(j, 0);
+      dma(j, smem0);
       wait_vmem();
     } else {
       gload(j);
-      sstore(0);
+      sstore(smem0);
     }
   }
   __syncthreads();
 
-  while (j < ntiles) {
+  auto step = [&](auto rb_tag) {
+    constexpr int RB_ = decltype(rb_tag)::value;
+    T* const rd = RB_ == 0 ? smem0 : smem1;
+    T* const nx = RB_ == 0 ? smem1 : smem0;
     const int jn = next_kept(j);
     if constexpr (S::DMA)
-      dma(jn < ntiles ? jn : j, cur ^ 1);  // buffer cur ^ 1 was last read before the previous barrier
+      dma(jn < ntiles ? jn : j, nx);  // nx was last read before the previous barrier
     else
       gload(jn < ntiles ? jn : j);  // unconditional prefetch (see the forward kernel)
-    const T* Ks = &smem[cur][0];
-    const T* Vs = &smem[cur][TILE];
+    const T* Ks = rd;
+    const T* Vs = rd + TILE;
     const int k0 = j * BC;
     const bool active = (q0w < N) && (!a.causal || k0 <= q0w + 31);
     if (active) {
@@ -278,8 +291,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             const frag b = frag4<T>(pack2<T>(s[kb][8 * hf + 0], s[kb][8 * hf + 1]), pack2<T>(s[kb][8 * hf + 2], s[kb][8 * hf + 3]),
                                     pack2<T>(s[kb][8 * hf + 4], s[kb][8 * hf + 5]), pack2<T>(s[kb][8 * hf + 6], s[kb][8 * hf + 7]));
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-              dq[db] = M::run(S::tr(Ks, kb * 32 + 16 * hf, db * 32, lane), b, dq[db]);
+            for (int db = 0; db < NDB; ++db) {
+              if constexpr (S::DMA)
+                dq[db] = M::run(load_frag_tr_lane<T, D>(Ks, kb * 32 + 16 * hf, trl[db]), b, dq[db]);
+              else
+                dq[db] = M::run(S::tr(Ks, kb * 32 + 16 * hf, db * 32, lane), b, dq[db]);
+            }
           }
       } else {
 #pragma unroll
@@ -293,12 +310,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
       }
     }
     if constexpr (S::DMA)
-      wait_vmem();  // this wave's loads into buffer cur ^ 1 have landed
+      wait_vmem();  // this wave's loads into nx have landed
     else
-      sstore(cur ^ 1);
+      sstore(nx);
     __syncthreads();
-    cur ^= 1;
     j = jn;
+  };
+  while (j < ntiles) {
+    step(std::integral_constant<int, 0>{});
+    if (j >= ntiles) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   const float sc = DROP ? a.scale * a.rp : a.scale;
@@ -309,8 +330,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     // rows start on distinct bank quads.
     constexpr int RS = 32 + 4;
     constexpr int WAVE_FLOATS = 32 * RS;
-    static_assert(sizeof(smem) >= 4 * WAVE_FLOATS * sizeof(float), "staging space in the tile buffers");
-    float* st = reinterpret_cast<float*>(&smem[0][0]) + w * WAVE_FLOATS;
+    static_assert(sizeof(smem0) >= 2 * WAVE_FLOATS * sizeof(float), "staging space in each tile buffer");
+    float* st = reinterpret_cast<float*>(w < 2 ? smem0 : smem1) + (w & 1) * WAVE_FLOATS;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll

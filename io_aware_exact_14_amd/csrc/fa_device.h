@@ -271,6 +271,36 @@ __device__ __forceinline__ typename Mfma<T>::frag load_frag_tr_swz(const T* tile
   return __builtin_bit_cast(typename Mfma<T>::frag, xy);
 }
 
+// load_frag_tr_swz split into a lane part and a row part. The lane part
+// (element offsets of the fragment's two reads for base row 0 and columns
+// col0...) depends only on the lane, because the swizzle depends on the row
+// modulo 16 and base is a multiple of 16; the row part is base * D, a
+// compile-time constant. tr_swz_lane returns the lane part through an
+// identity DPP move, which the optimizer cannot look through: every read's
+// address is then "tile + lane part + constant", a short chain from the LDS
+// array, and the compiler keeps the array's alias scope on the read. With
+// the scope it can tell the reads apart from direct-to-LDS loads into
+// another array instead of waiting for those loads to land.
+template <typename T, int D>
+__device__ __forceinline__ int2 tr_swz_lane(int col0, int lane) {
+  static_assert(sizeof(T) == 2, "16-bit only");
+  const int j = lane & 15;
+  const int row = 4 * (lane >> 5) + (j >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const int o0 = row * D + (((col >> 3) ^ lds_swizzle<D>(row)) << 3) + (col & 7);
+  const int o1 = (row + 8) * D + (((col >> 3) ^ lds_swizzle<D>(row + 8)) << 3) + (col & 7);
+  return make_int2(__builtin_amdgcn_mov_dpp(o0, 0xE4, 0xF, 0xF, false),
+                   __builtin_amdgcn_mov_dpp(o1, 0xE4, 0xF, 0xF, false));
+}
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma<T>::frag load_frag_tr_lane(const T* tile, int base, int2 lo) {
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + lo.x + base * D));
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + lo.y + base * D));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 xy = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(typename Mfma<T>::frag, xy);
+}
+
 // Whether byte `idx` of a block mask is nonzero. `idx` must be uniform across
 // the wave: the aligned dword holding the byte is read with a scalar load
 // (constant address space), which keeps the vector-memory counter free for

@@ -82,7 +82,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   constexpr int RB = D * (int)sizeof(T);  // bytes per row
   constexpr float NEG_INF = -__builtin_inff();
 
-  __shared__ __attribute__((aligned(16))) T smem[2][2 * C::TILE];  // [buffer][K tile | V tile], row-major
+  // The two tile buffers, each [K tile | V tile] row-major, are separate
+  // arrays and the tile loop below is unrolled by two, so every access names
+  // its buffer at compile time. The compiler can then tell the direct-to-LDS
+  // loads into one buffer from the reads of the other; with one indexed array
+  // it waits for those loads before the first transpose read of each tile.
+  __shared__ __attribute__((aligned(16))) T smem0[2 * C::TILE];
+  __shared__ __attribute__((aligned(16))) T smem1[2 * C::TILE];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, lo = lane & 31, hi = lane >> 5;
@@ -163,7 +169,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
   // address (M0) is scalar arithmetic rather than a vector value moved to a
   // scalar register per load.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto dma = [&](int jt, int buf) {
+  auto dma = [&](int jt, T* dst) {
     const int k0 = jt * BC;
     const int rem = (N - k0) * RB;
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (size_t)k0 * D, rem);
@@ -171,8 +177,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i) {
       const int c0 = i * 256 + wu * 64;  // first chunk this wave writes
-      buffer_load16_lds(kr, &smem[buf][c0 * C::EPC], voff[i]);
-      buffer_load16_lds(vr, &smem[buf][C::TILE + c0 * C::EPC], voff[i]);
+      buffer_load16_lds(kr, dst + c0 * C::EPC, voff[i]);
+      buffer_load16_lds(vr, dst + C::TILE + c0 * C::EPC, voff[i]);
     }
   };
   auto gload = [&](int jt) {
@@ -186,13 +192,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
       vreg[i] = buffer_load16(vr, voff[i]);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](T* dst) {
 #pragma unroll
     for (int i = 0; i < (C::DMA ? 1 : C::NLD); ++i) {
       const int c = i * 256 + tid;
       const int row = lds_row(c / C::KCH), ch = c % C::KCH;
-      *reinterpret_cast<u32x4*>(&smem[buf][row * C::KS + ch * C::EPC]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&smem[buf][C::TILE + row * C::KS + ch * C::EPC]) = vreg[i];
+      *reinterpret_cast<u32x4*>(dst + row * C::KS + ch * C::EPC) = kreg[i];
+      *reinterpret_cast<u32x4*>(dst + C::TILE + row * C::KS + ch * C::EPC) = vreg[i];
     }
   };
 
@@ -206,31 +212,42 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     for (int db = 0; db < NDB; ++db) o[b][db] = zero16();
   }
 
+  // Lane parts of the V^T transpose-read addresses (swizzled tiles).
+  int2 trl[C::DMA ? NDB : 1];
+  if constexpr (C::DMA) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) trl[db] = tr_swz_lane<T, D>(db * 32, lane);
+  }
+
   int j = kept(0) ? 0 : next_kept(0);
-  int cur = 0;
   if (j < ntiles) {
     if constexpr (C::DMA) {
-      dma(j, 0);
+      dma(j, smem0);
       wait_vmem();
     } else {
       gload(j);
-      sstore(0);
+      sstore(smem0);
     }
   }
   __syncthreads();
 
-  while (j < ntiles) {
+  // One tile step: compute on buffer RB while the next tile loads into the
+  // other one.
+  auto step = [&](auto rb_tag) {
+    constexpr int RB_ = decltype(rb_tag)::value;
+    T* const rd = RB_ == 0 ? smem0 : smem1;
+    T* const nx = RB_ == 0 ? smem1 : smem0;
     const int jn = next_kept(j);
     // Always prefetch (the last iteration reloads its own tile into the idle
     // buffer), so the loads are unconditional and the compiler's wait
     // counting keeps them in flight across the compute below.
     if constexpr (C::DMA)
-      dma(jn < ntiles ? jn : j, cur ^ 1);  // buffer cur ^ 1 was last read before the previous barrier
+      dma(jn < ntiles ? jn : j, nx);  // nx was last read before the previous barrier
     else
       gload(jn < ntiles ? jn : j);
 
-    const T* Ks = &smem[cur][0];
-    const T* Vs = &smem[cur][C::TILE];
+    const T* Ks = rd;
+    const T* Vs = rd + C::TILE;
     const int k0 = j * BC;
     // The wave has work unless every key of the tile is above all its rows.
     const bool active = (q0b[0] < N) && (!a.causal || k0 <= qlast);
@@ -375,7 +392,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
             for (int db = 0; db < NDB; ++db) {
               frag vt;
               if constexpr (C::DMA)
-                vt = load_frag_tr_swz<T, D>(Vs, kb * 32 + 16 * hf, db * 32, lane);
+                vt = load_frag_tr_lane<T, D>(Vs, kb * 32 + 16 * hf, trl[db]);
               else
                 vt = load_frag_tr_rp<T>(Vs, C::KS, kb * 32 + 16 * hf, db * 32, lane);
 #pragma unroll
@@ -399,12 +416,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     }
 
     if constexpr (C::DMA)
-      wait_vmem();  // this wave's loads into buffer cur ^ 1 have landed
+      wait_vmem();  // this wave's loads into nx have landed
     else
-      sstore(cur ^ 1);
+      sstore(nx);
     __syncthreads();
-    cur ^= 1;
     j = jn;
+  };
+  while (j < ntiles) {
+    step(std::integral_constant<int, 0>{});
+    if (j >= ntiles) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(static_cast<T*>(a.out) + hoff, N * RB);
@@ -419,8 +440,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     typedef T t4 __attribute__((ext_vector_type(4)));
     constexpr int RSE = D + 8;
     constexpr int WAVE_ELTS = 32 * RSE;
-    static_assert(sizeof(smem) >= 4 * WAVE_ELTS * sizeof(T), "staging space in the tile buffers");
-    T* st = &smem[0][0] + w * WAVE_ELTS;
+    static_assert(sizeof(smem0) >= 4 * WAVE_ELTS * sizeof(T), "staging space in the first tile buffer");
+    T* st = smem0 + w * WAVE_ELTS;
     const float lt = half_sum(l_run[0]);
     const float inv = lt > 0.f ? a.rp / lt : 0.f;
 #pragma unroll
