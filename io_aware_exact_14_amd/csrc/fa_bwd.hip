@@ -517,169 +517,34 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WP
   }
 
   int it = nqt - 1 >= istart && kept(nqt - 1) ? nqt - 1 : prev_kept(nqt - 1);
-  int cur = 0;
   if (it >= istart) {
     gload(it);
     sstore(0);
   }
   __syncthreads();
 
-  while (it >= istart) {
-    const int itn = prev_kept(it);
-    // Unconditional prefetch (see the forward kernel). At d = 128 it is
-    // issued after the tile's S and dP products rather than ahead of them:
-    // the products then start without waiting behind the loads' issue
-    // (dK/dV -2% at 16K keys; at d = 64 it measured even or slower, and
-    // with dropout at d = 128 it costs a spilled register).
-    constexpr bool kLateLoad = D == 128 && KH == 8 && !DROP;
-    const int itl = itn >= istart ? itn : it;
-    if constexpr (!kLateLoad) gload(itl);
-    const T* Qs = &smem[cur][0];
-    const T* dOs = &smem[cur][TILE];
-    const int i0 = it * BR;
-    // The wave has work unless every query of the tile is above its keys.
-    const bool active = (k0w < N) && (!a.causal || i0 + BR - 1 >= k0w);
-    if (active) {
-      // One tile step. With two query blocks it is instantiated with and
-      // without the diagonal / end masking, so the unmasked step (almost
-      // every tile) is one basic block that the compiler schedules as a
-      // whole, and the keep bits go first (they depend on nothing the MFMAs
-      // produce); each block's softmax then follows its own products. With
-      // one query block a single instance masks at run time, which keeps
-      // its register use within the occupancy target.
-      constexpr bool kPipe = NQB == 2 && KH == 8;
-      const bool need_mask = (a.causal && i0 < k0w + 31) || (k0w + 31 >= N);
-      auto step = [&](auto mask_tag) {
-        constexpr int kMask = decltype(mask_tag)::value;  // 0: no mask, 1: mask, 2: need_mask decides
-        bool kbit[NQB][16];  // keep bit of element v (dropout only)
-        auto keep_bits = [&](int qb) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            // Elements 4g + 2t, 4g + 2t + 1 are rows r, r + 1 (r = qb*32 + 8g + 4hi + 2t).
-            const u32x2 h2 = *reinterpret_cast<const u32x2*>(&side_h[cur][qb * 32 + 8 * g + 4 * hi + 2 * (int)odd]);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const uint32_t own = keep_finish(h2[t] + keyh);  // row r + odd
-              // quad_perm [1, 0, 3, 2]: the neighbour's word, row r + 1 - odd
-              const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, true);
-              const uint32_t x = __builtin_amdgcn_perm(nb, own, psel);
-              kbit[qb][4 * g + 2 * t] = (uint16_t)x >= (uint16_t)t16;
-              kbit[qb][4 * g + 2 * t + 1] = x >= a.thresh;
-            }
-          }
-        };
-        if constexpr (DROP && kPipe) {
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) keep_bits(qb);
-        }
-        f32x16 s[NQB], dp[NQB];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          s[qb] = zero16();
-          if constexpr (DROP) {
-            dp[qb] = zero16();
-          } else {
-            // Start the product from -D of each element's query: it then yields dP - D.
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&side_d[cur][qb * 32 + 8 * g + 4 * hi]);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) dp[qb][4 * g + e] = d4[e];
-            }
-          }
-        }
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int off = S::at(qb * 32 + lo, c * KI + hi * KH);
-            s[qb] = M::run(load_frag<T>(Qs + off), kf[c], s[qb]);
-            if constexpr (VLDS)
-              dp[qb] = M::run(load_frag<T>(dOs + off), load_frag<T>(&vsm[(w * 32 + lo) * S::KS + c * KI + hi * KH]),
-                              dp[qb]);
-            else
-              dp[qb] = M::run(load_frag<T>(dOs + off), vf[c], dp[qb]);
-          }
-        if constexpr (kLateLoad) gload(itl);
-        if (kMask == 1 || (kMask == 2 && need_mask)) {
-          // Hide queries below this lane's key (causal), or every query when
-          // the key is past the end: query - i0 is a compile-time offset plus
-          // 4*hi, so each element costs one compare.
-          const int t = (kvalid ? (a.causal ? key - i0 : -(1 << 30)) : (1 << 30)) - 4 * hi;
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if (qb * 32 + 8 * (v >> 2) + (v & 3) < t) s[qb][v] = NEG_INF;
-        }
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          if constexpr (DROP && !kPipe) keep_bits(qb);
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int ql = qb * 32 + 8 * g + 4 * hi;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&side_l[cur][ql]);
-            f32x4 nd4 = {0.f, 0.f, 0.f, 0.f};  // -D'
-            if constexpr (DROP) nd4 = *reinterpret_cast<const f32x4*>(&side_d[cur][ql]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int v = 4 * g + e;
-              const float p = exp2_fast(fmaf(s[qb][v], a.sl2, -l4[e]));
-              if constexpr (DROP) {
-                // dS' = P * (Z * dP - D') = P Z dP - P D', D' = D (1 - p); the
-                // factors 1 / (1 - p) go on dK and dV at the end.
-                const float pz = kbit[qb][v] ? p : 0.f;
-                s[qb][v] = pz;
-                dp[qb][v] = fmaf(pz, dp[qb][v], p * nd4[e]);
-              } else {
-                s[qb][v] = p;
-                dp[qb][v] = p * dp[qb][v];  // the products started from -D: dS = P * (dP - D)
-              }
-            }
-          }
-          if constexpr (KH == 8) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              const frag bp = frag4<T>(pack2<T>(s[qb][8 * hf + 0], s[qb][8 * hf + 1]), pack2<T>(s[qb][8 * hf + 2], s[qb][8 * hf + 3]),
-                                       pack2<T>(s[qb][8 * hf + 4], s[qb][8 * hf + 5]), pack2<T>(s[qb][8 * hf + 6], s[qb][8 * hf + 7]));
-              const frag bs = frag4<T>(pack2<T>(dp[qb][8 * hf + 0], dp[qb][8 * hf + 1]), pack2<T>(dp[qb][8 * hf + 2], dp[qb][8 * hf + 3]),
-                                       pack2<T>(dp[qb][8 * hf + 4], dp[qb][8 * hf + 5]), pack2<T>(dp[qb][8 * hf + 6], dp[qb][8 * hf + 7]));
-              const int base = qb * 32 + 16 * hf;
-#pragma unroll
-              for (int db = 0; db < NDB; ++db) {
-                dv[db] = M::run(S::tr(dOs, base, db * 32, lane), bp, dv[db]);
-                dk[db] = M::run(S::tr(Qs, base, db * 32, lane), bs, dk[db]);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int ql = S::at(qb * 32 + crow(v, hi), 0);
-#pragma unroll
-              for (int db = 0; db < NDB; ++db) {
-                dv[db] = M::run(dOs[ql + db * 32 + lo], s[qb][v], dv[db]);
-                dk[db] = M::run(Qs[ql + db * 32 + lo], dp[qb][v], dk[db]);
-              }
-            }
-          }
-        }
-      };
-      if constexpr (kPipe) {
-        if (need_mask)
-          step(std::integral_constant<int, 1>{});
-        else
-          step(std::integral_constant<int, 0>{});
-      } else {
-        step(std::integral_constant<int, 2>{});
+  // The loop body is in fa_bwd_dkdv_tile.inc. At d = 64 with one query
+  // block per tile the loop is unrolled by two, so every access names its
+  // buffer at compile time (C2 dK/dV -2%); with two query blocks that spills
+  // registers, and the d = 128 kernels keep the plain loop.
+  if constexpr (D == 64 && NQB == 1) {
+    while (it >= istart) {
+      {
+        constexpr int cur = 0;
+#include "fa_bwd_dkdv_tile.inc"
+      }
+      if (it < istart) break;
+      {
+        constexpr int cur = 1;
+#include "fa_bwd_dkdv_tile.inc"
       }
     }
-    if constexpr (kLateLoad) {
-      if (!active) gload(itl);
+  } else {
+    int cur = 0;
+    while (it >= istart) {
+#include "fa_bwd_dkdv_tile.inc"
+      cur ^= 1;
     }
-    sstore(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
-    it = itn;
   }
 
   const float sc = DROP ? a.scale * a.rp : a.scale;  // dK = scale * sum_i dS'_ij Q_i / (1 - p)
