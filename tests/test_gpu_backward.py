@@ -187,3 +187,12 @@ def test_block_mask_wider_than_64_blocks(fa):
     N, mb = 8400, 128
     bm = random_block_mask((N + mb - 1) // mb, seed=66, frac=0.1)
     _check_bwd(fa, 1, 1, N, 64, torch.bfloat16, causal=False, bm=bm, mb=mb, in_seed=8400)
+
+
+# The same for the backward loops (unrolled by two in the dQ kernel, and in
+# the dK/dV kernel at d = 64 with 32-row query tiles): 1, 3, 5 and 6 tiles
+# of 32 rows or keys, and 1 to 3 of 64.
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_tile_count_parity(fa, d):
+    for N in (32, 96, 160, 192):
+        _check_bwd(fa, 2, 4, N, d, torch.bfloat16, causal=False, in_seed=N + 6)

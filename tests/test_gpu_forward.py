@@ -142,3 +142,13 @@ def test_forward_deterministic(fa):
     o2, l2 = fa.forward(qd, kd, vd, causal=True, dropout_p=0.2, seed=5)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# The forward tile loop is unrolled by two (each step's LDS buffers fixed at
+# compile time), so whether a workgroup's tile count is odd or even decides
+# which copy ends the loop. Non-causal, 64-key tiles, a grid wide enough
+# for the 128-row kernel: 1, 2, 3 and 5 tiles per workgroup.
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_tile_count_parity(fa, d):
+    for N in (64, 128, 192, 320):
+        _check_fwd(fa, 4, 17, N, d, torch.bfloat16, causal=False, in_seed=N + 5)
