@@ -240,11 +240,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
     const int jn = next_kept(j);
     // Always prefetch (the last iteration reloads its own tile into the idle
     // buffer), so the loads are unconditional and the compiler's wait
-    // counting keeps them in flight across the compute below.
-    if constexpr (C::DMA)
-      dma(jn < ntiles ? jn : j, nx);  // nx was last read before the previous barrier
-    else
-      gload(jn < ntiles ? jn : j);
+    // counting keeps them in flight across the compute below. nx was last
+    // read before the previous barrier. Direct-to-LDS loads go out after the
+    // S products, so the K fragment reads that open the step do not share
+    // the LDS with their writes (C4 forward -2.3 to -3.2%).
+    const int jl = jn < ntiles ? jn : j;
+    if constexpr (!C::DMA) gload(jl);
 
     const T* Ks = rd;
     const T* Vs = rd + C::TILE;
@@ -273,6 +274,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
           for (int b = 0; b < QB; ++b) s[b][kb] = M::run(kf, qf[b][c], s[b][kb]);
         }
       }
+      if constexpr (C::DMA) dma(jl, nx);
 
 #pragma unroll
       for (int b = 0; b < QB; ++b) {
@@ -415,10 +417,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
       }
     }
 
-    if constexpr (C::DMA)
+    if constexpr (C::DMA) {
+      if (!active) dma(jl, nx);
       wait_vmem();  // this wave's loads into nx have landed
-    else
+    } else {
       sstore(nx);
+    }
     __syncthreads();
     j = jn;
   };
